@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Conv2D -> BatchNorm -> ReLU operator on one MI355X.
+
+One step = one cbr_forward_train call (conv + channel statistics, finalize, normalise +
+ReLU + mask) on the headline workload: N=256, 56x56, 64 -> 64 channels, 3x3, stride 1,
+pad 1, bf16 NHWC, inputs resident in HBM.  The timed region is exactly --steps calls,
+bracketed by device synchronisation; per-kernel durations come from HIP events the
+library records on its stream inside the same region.
+
+Printed: one JSON line with the step throughput (TFLOP/s of the convolution, plus
+algorithmic HBM GB/s), the roofline of the dominant kernel, the other calls' kernels
+(inference and backward workloads, unless --no-aux), and the fp64 CPU oracle timed on
+the host as a reported baseline (unless --no-cpu-baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+BF16 = 2
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def conv_flops(g):
+    """2 * M * K * R * S * C: multiply-adds of the convolution only."""
+    return 2.0 * g.m * g.k * g.r * g.s * g.c
+
+
+def train_bytes(g):
+    """Algorithmic HBM bytes of the fused training forward, per kernel.
+    conv: read x and w, write z; apply: read z, write y and the packed mask."""
+    x = g.n * g.h * g.w * g.c * BF16
+    w = g.k * g.r * g.s * g.c * BF16
+    z = g.m * g.k * BF16
+    mask = (g.m * g.k + 31) // 32 * 4
+    return {"conv_fprop_stats": x + w + z, "bn_stats_finalize": 0, "bn_apply_relu_mask": z + z + mask}
+
+
+def unfused_train_bytes(g):
+    """Three-kernel baseline: conv writes z; BN reads z for statistics, reads it again
+    and writes its output; ReLU reads that and writes y plus a one-byte-per-element mask."""
+    x = g.n * g.h * g.w * g.c * BF16
+    w = g.k * g.r * g.s * g.c * BF16
+    z = g.m * g.k * BF16
+    return x + w + z + (z + z + z) + (z + z + g.m * g.k)
+
+
+def infer_bytes(g):
+    x = g.n * g.h * g.w * g.c * BF16
+    w = g.k * g.r * g.s * g.c * BF16
+    y = g.m * g.k * BF16
+    return {"bn_fold": w + w, "conv_fprop_bias_relu": x + w + y}
+
+
+def bwd_bytes(g):
+    x = g.n * g.h * g.w * g.c * BF16
+    w = g.k * g.r * g.s * g.c * BF16
+    z = g.m * g.k * BF16
+    mask = (g.m * g.k + 31) // 32 * 4
+    dw = g.k * g.r * g.s * g.c * 4
+    # BN backward: reduce reads dy, mask, z; apply reads them again and writes dz.
+    return {"bn_backward": (z + mask + z) * 2 + z, "conv_wgrad": z + x + dw, "conv_dgrad": z + w + x}
+
+
+def kernel_entry(name, ms, nbytes, flops):
+    t = ms * 1e-3
+    gbs = nbytes / t / 1e9 if t > 0 else 0.0
+    tfl = flops / t / 1e12 if t > 0 else 0.0
+    return {"kernel": name, "ms": round(ms, 5), "gbps": round(gbs, 1), "tflops": round(tfl, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bytes": int(nbytes), "flops": int(flops)}
+
+
+def roofline_of(entry):
+    """The kernel's binding roofline: whichever of HBM bytes and MFMA flops needs more
+    time at peak."""
+    t_hbm = entry["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = entry["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        return {"kernel": entry["kernel"], "bound": "mfma", "achieved": entry["tflops"],
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": entry["mfma_frac"], "traffic": None}
+    return {"kernel": entry["kernel"], "bound": "hbm", "achieved": entry["gbps"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": entry["hbm_frac"], "traffic": None}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-aux", action="store_true", help="skip the inference and backward workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-images", type=int, default=256,
+                    help="images of the headline workload the CPU oracle runs (of 256)")
+    ap.add_argument("--cold", type=int, default=5, help="steps timed after evicting the caches")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported here (this operator's "
+              "multi-GPU form is data parallelism over the batch; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import conv2d_batchnorm_relu_amd as cbr
+    from conv2d_batchnorm_relu_amd.inputs import draw_workload, bf16_bits
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_bf16(a):
+        return torch.from_numpy(bf16_bits(a).view(np.int16)).to(dev)
+
+    def to_f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def shape_of(g):
+        return cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.pad)
+
+    def make_event():
+        # torch creates the underlying hipEvent_t on first record; the library then
+        # re-records it on its own stream.
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def timed(fn, nev, steps, warmup):
+        """Runs fn(events) warmup + steps times; returns (wall ms/step, [per-stage ms])."""
+        for _ in range(warmup):
+            fn(None)
+        evs = [[make_event() for _ in range(nev)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        stages = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+                  for j in range(nev - 1)]
+        return wall, stages
+
+    # ---------------- headline: training forward ----------------
+    log("drawing the headline workload")
+    wl, d = draw_workload("s2_train")
+    g = wl.geom
+    sp = shape_of(g)
+    x, w = to_bf16(d["x"]), to_bf16(d["w"])
+    gamma, beta = to_f32(d["gamma"]), to_f32(d["beta"])
+    rm, rv = to_f32(d["run_mean"]), to_f32(d["run_var"])
+    z = torch.empty((g.n, g.p, g.q, g.k), dtype=torch.int16, device=dev)
+    y = torch.empty_like(z)
+    mask = torch.empty(cbr.cbr_mask_words(sp), dtype=torch.int32, device=dev)
+    sm, si = torch.empty(g.k, device=dev), torch.empty(g.k, device=dev)
+    rmo, rvo = torch.empty(g.k, device=dev), torch.empty(g.k, device=dev)
+    ws = torch.empty(cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_TRAIN), dtype=torch.uint8, device=dev)
+
+    def train_step(events):
+        cbr.cbr_forward_train(sp, x, w, gamma, beta, rm, rv, wl.eps, wl.momentum, z, y, mask, sm, si,
+                              rmo, rvo, ws, events=events)
+
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms, stages = timed(train_step, 4, args.steps, args.warmup)
+    flops = conv_flops(g)
+    kb = train_bytes(g)
+    kernels = [kernel_entry("conv_fprop_stats", stages[0], kb["conv_fprop_stats"], flops),
+               kernel_entry("bn_stats_finalize", stages[1], 0, 0),
+               kernel_entry("bn_apply_relu_mask", stages[2], kb["bn_apply_relu_mask"], 0)]
+    dominant = max(kernels, key=lambda e: e["ms"])
+    total_bytes = sum(kb.values())
+
+    # cold steps: evict the 256 MB last-level cache before each one
+    cold = []
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold):
+            flush.fill_(1)
+            ev = [make_event() for _ in range(4)]
+            train_step(ev)
+            torch.cuda.synchronize()
+            cold.append([ev[j].elapsed_time(ev[j + 1]) for j in range(3)])
+        del flush
+    cold_ms = float(np.median([sum(c) for c in cold])) if cold else None
+
+    out = {
+        "metric": "CBR train-fwd TFLOP/s + HBM GB/s (% roofline), N256 56x56 64->64 3x3 bf16",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "train forward N256 56x56 C64->K64 3x3 s1 p1 bf16 NHWC",
+                   "n": g.n, "h": g.h, "w": g.w, "c": g.c, "k": g.k, "r": g.r, "s": g.s,
+                   "stride": g.stride, "pad": g.pad, "seed": wl.seed},
+        "gbps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_roofline_frac": round(total_bytes / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4),
+        "bytes_per_step": int(total_bytes),
+        "unfused_bytes": int(unfused_train_bytes(g)),
+        "roofline": roofline_of(dominant),
+        "kernels": kernels,
+        "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
+    }
+    del z, y, mask, ws, x
+    torch.cuda.empty_cache()
+
+    # ---------------- other calls ----------------
+    if not args.no_aux:
+        aux = {}
+        steps = max(10, args.steps // 5)
+        log("inference workload")
+        wl4, d4 = draw_workload("s3_infer")
+        g4 = wl4.geom
+        sp4 = shape_of(g4)
+        t4 = dict(x=to_bf16(d4["x"]), w=to_bf16(d4["w"]), b=to_f32(d4["bias"]), ga=to_f32(d4["gamma"]),
+                  be=to_f32(d4["beta"]), rm=to_f32(d4["run_mean"]), rv=to_f32(d4["run_var"]),
+                  y=torch.empty((g4.n, g4.p, g4.q, g4.k), dtype=torch.int16, device=dev),
+                  ws=torch.empty(cbr.cbr_workspace_bytes(sp4, cbr.CBR_OP_INFER), dtype=torch.uint8, device=dev))
+
+        def infer_step(events):
+            cbr.cbr_forward_infer(sp4, t4["x"], t4["w"], t4["b"], t4["ga"], t4["be"], t4["rm"], t4["rv"],
+                                  wl4.eps, t4["y"], t4["ws"], events=events)
+
+        ms4, st4 = timed(infer_step, 3, steps, 5)
+        ib = infer_bytes(g4)
+        aux["infer"] = {"workload": "infer N256 28x28 C128->K128 3x3 s1 p1 (conv bias)", "ms": round(ms4, 5),
+                        "tflops": round(conv_flops(g4) / (ms4 * 1e-3) / 1e12, 2),
+                        "kernels": [kernel_entry("bn_fold", st4[0], ib["bn_fold"], 0),
+                                    kernel_entry("conv_fprop_bias_relu", st4[1], ib["conv_fprop_bias_relu"],
+                                                 conv_flops(g4))]}
+        del t4
+        log("backward workload")
+        wl5, d5 = draw_workload("s4_bwd")
+        g5 = wl5.geom
+        sp5 = shape_of(g5)
+        t5 = dict(x=to_bf16(d5["x"]), w=to_bf16(d5["w"]), ga=to_f32(d5["gamma"]), be=to_f32(d5["beta"]),
+                  rm=to_f32(d5["run_mean"]), rv=to_f32(d5["run_var"]), dy=to_bf16(d5["dy"]))
+        zz = torch.empty((g5.n, g5.p, g5.q, g5.k), dtype=torch.int16, device=dev)
+        yy = torch.empty_like(zz)
+        mk = torch.empty(cbr.cbr_mask_words(sp5), dtype=torch.int32, device=dev)
+        s5m, s5i = torch.empty(g5.k, device=dev), torch.empty(g5.k, device=dev)
+        r5m, r5v = torch.empty(g5.k, device=dev), torch.empty(g5.k, device=dev)
+        ws5 = torch.empty(max(cbr.cbr_workspace_bytes(sp5, cbr.CBR_OP_TRAIN),
+                              cbr.cbr_workspace_bytes(sp5, cbr.CBR_OP_BWD)), dtype=torch.uint8, device=dev)
+
+        def fwd5(events):
+            cbr.cbr_forward_train(sp5, t5["x"], t5["w"], t5["ga"], t5["be"], t5["rm"], t5["rv"], wl5.eps,
+                                  wl5.momentum, zz, yy, mk, s5m, s5i, r5m, r5v, ws5, events=events)
+
+        fwd5(None)
+        dz = torch.empty_like(zz)
+        dgam, dbet = torch.empty(g5.k, device=dev), torch.empty(g5.k, device=dev)
+        dw = torch.empty((g5.k, g5.r, g5.s, g5.c), device=dev)
+        dx = torch.empty((g5.n, g5.h, g5.w, g5.c), dtype=torch.int16, device=dev)
+
+        def bwd_step(events):
+            cbr.cbr_backward(sp5, t5["x"], t5["w"], zz, mk, t5["dy"], t5["ga"], s5m, s5i, dz, dgam, dbet, dw,
+                             dx, ws5, events=events)
+
+        ms5, st5 = timed(bwd_step, 4, steps, 5)
+        bb = bwd_bytes(g5)
+        f5 = conv_flops(g5)
+        aux["backward"] = {"workload": "backward N256 14x14 C256->K256 3x3 s1 p1", "ms": round(ms5, 5),
+                           "tflops": round(2 * f5 / (ms5 * 1e-3) / 1e12, 2),
+                           "kernels": [kernel_entry("bn_backward", st5[0], bb["bn_backward"], 0),
+                                       kernel_entry("conv_wgrad", st5[1], bb["conv_wgrad"], f5),
+                                       kernel_entry("conv_dgrad", st5[2], bb["conv_dgrad"], f5)]}
+        ms5f, st5f = timed(fwd5, 4, steps, 5)
+        aux["train_s4"] = {"workload": "train forward N256 14x14 C256->K256 3x3", "ms": round(ms5f, 5),
+                           "tflops": round(f5 / (ms5f * 1e-3) / 1e12, 2)}
+        del t5, zz, yy, mk, ws5, dz, dx
+        torch.cuda.empty_cache()
+        log("first-layer workload")
+        wl2, d2 = draw_workload("stem")
+        g2 = wl2.geom
+        sp2 = shape_of(g2)
+        t2 = dict(x=to_bf16(d2["x"]), w=to_bf16(d2["w"]), ga=to_f32(d2["gamma"]), be=to_f32(d2["beta"]),
+                  rm=to_f32(d2["run_mean"]), rv=to_f32(d2["run_var"]))
+        z2 = torch.empty((g2.n, g2.p, g2.q, g2.k), dtype=torch.int16, device=dev)
+        y2 = torch.empty_like(z2)
+        m2 = torch.empty(cbr.cbr_mask_words(sp2), dtype=torch.int32, device=dev)
+        v2 = [torch.empty(g2.k, device=dev) for _ in range(4)]
+        ws2 = torch.empty(cbr.cbr_workspace_bytes(sp2, cbr.CBR_OP_TRAIN), dtype=torch.uint8, device=dev)
+
+        def stem_step(events):
+            cbr.cbr_forward_train(sp2, t2["x"], t2["w"], t2["ga"], t2["be"], t2["rm"], t2["rv"], wl2.eps,
+                                  wl2.momentum, z2, y2, m2, v2[0], v2[1], v2[2], v2[3], ws2, events=events)
+
+        ms2, st2 = timed(stem_step, 4, steps, 5)
+        kb2 = train_bytes(g2)
+        aux["stem_train"] = {"workload": "train forward N64 224x224 C3->K64 7x7 s2 p3", "ms": round(ms2, 5),
+                             "gbps": round(sum(kb2.values()) / (ms2 * 1e-3) / 1e9, 1),
+                             "kernels": [kernel_entry("conv_fprop_stats(first layer)", st2[0],
+                                                      kb2["conv_fprop_stats"], conv_flops(g2)),
+                                         kernel_entry("bn_stats_finalize", st2[1], 0, 0),
+                                         kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0)]}
+        del t2, z2, y2, m2, ws2
+        out["aux"] = aux
+
+    # ---------------- CPU baseline: the fp64 oracle on the host ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+        n = max(1, min(args.cpu_images, g.n))
+        log(f"CPU oracle on {n} of {g.n} images")
+        sub = {k: (v[:n] if k == "x" else v) for k, v in d.items()}
+        gs = g.with_n(n)
+        osp = oracle.OShape(gs.n, gs.h, gs.w, gs.c, gs.k, gs.r, gs.s, gs.stride, gs.stride, gs.pad, gs.pad)
+        t0 = time.perf_counter()
+        oracle.forward_train(osp, sub["x"], sub["w"], sub["gamma"], sub["beta"], sub["run_mean"],
+                             sub["run_var"], wl.eps, wl.momentum)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(conv_flops(gs) / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"train forward on {n} of {g.n} images of the headline workload "
+                                         f"(fp64 direct loops), {dt:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

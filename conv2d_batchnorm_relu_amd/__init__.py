@@ -1,0 +1,177 @@
+"""Fused Conv2D -> BatchNorm -> ReLU (CBR) for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libcbr.so`` (the HIP kernels and the C ABI declared in
+``include/cbr.h``).  The functions carry the C names and only marshal arguments: torch
+tensors are passed by device pointer, the stream defaults to torch's current stream.
+All computation runs in the library's kernels; there is no CPU path, and every call
+raises if the library has not been built.
+
+Tensor conventions (see include/cbr.h): NHWC activations and KRSC filters as
+``torch.bfloat16`` (or 16-bit integer tensors holding bf16 bits), float32 per-channel
+vectors, an int32/uint32 packed ReLU mask of ``cbr_mask_words(shape)`` words, and a
+caller-allocated device workspace of ``cbr_workspace_bytes(shape, op)`` bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["CbrError", "CbrShape", "make_shape", "cbr_status_str", "cbr_output_hw", "cbr_mask_words",
+           "cbr_workspace_bytes", "cbr_forward_train", "cbr_forward_infer", "cbr_backward",
+           "CBR_OP_TRAIN", "CBR_OP_INFER", "CBR_OP_BWD", "library_path"]
+
+CBR_OP_TRAIN, CBR_OP_INFER, CBR_OP_BWD = 0, 1, 2
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcbr.so")
+
+
+class CbrShape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("n", "h", "w", "c", "k", "r", "s", "stride_h", "stride_w", "pad_h", "pad_w")]
+
+
+class CbrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {cbr_status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(the CBR operator has no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(CbrShape)
+    lib.cbr_status_str.argtypes = [ctypes.c_int]
+    lib.cbr_status_str.restype = ctypes.c_char_p
+    lib.cbr_output_hw.argtypes = [S, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.cbr_output_hw.restype = ctypes.c_int
+    lib.cbr_mask_words.argtypes = [S]
+    lib.cbr_mask_words.restype = ctypes.c_size_t
+    lib.cbr_workspace_bytes.argtypes = [S, ctypes.c_int]
+    lib.cbr_workspace_bytes.restype = ctypes.c_size_t
+    lib.cbr_forward_train.argtypes = [S, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                      P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.cbr_forward_train.restype = ctypes.c_int
+    lib.cbr_forward_infer.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    lib.cbr_forward_infer.restype = ctypes.c_int
+    lib.cbr_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.cbr_backward.restype = ctypes.c_int
+    lib.cbr_forward_train_ev.argtypes = lib.cbr_forward_train.argtypes + [P]
+    lib.cbr_forward_train_ev.restype = ctypes.c_int
+    lib.cbr_forward_infer_ev.argtypes = lib.cbr_forward_infer.argtypes + [P]
+    lib.cbr_forward_infer_ev.restype = ctypes.c_int
+    lib.cbr_backward_ev.argtypes = lib.cbr_backward.argtypes + [P]
+    lib.cbr_backward_ev.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_shape(n, h, w, c, k, r, s, stride=1, pad=0, stride_w=None, pad_w=None) -> CbrShape:
+    return CbrShape(n, h, w, c, k, r, s, stride, stride if stride_w is None else stride_w,
+                    pad, pad if pad_w is None else pad_w)
+
+
+def _sp(shape):
+    return ctypes.byref(shape)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != 0:
+        raise CbrError(status, where)
+
+
+def cbr_status_str(status: int) -> str:
+    return _load().cbr_status_str(int(status)).decode()
+
+
+def cbr_output_hw(shape: CbrShape):
+    p, q = ctypes.c_int32(), ctypes.c_int32()
+    _check(_load().cbr_output_hw(_sp(shape), ctypes.byref(p), ctypes.byref(q)), "cbr_output_hw")
+    return p.value, q.value
+
+
+def cbr_mask_words(shape: CbrShape) -> int:
+    return int(_load().cbr_mask_words(_sp(shape)))
+
+
+def cbr_workspace_bytes(shape: CbrShape, op: int) -> int:
+    return int(_load().cbr_workspace_bytes(_sp(shape), int(op)))
+
+
+def _events(events):
+    """A ctypes array of hipEvent_t handles (torch.cuda.Event objects or raw ints)."""
+    if events is None:
+        return None
+    handles = [e if isinstance(e, int) else e.cuda_event for e in events]
+    return (ctypes.c_void_p * len(handles))(*handles)
+
+
+def cbr_forward_train(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, momentum,
+                      z, y, relu_mask, saved_mean, saved_invstd, run_mean_out, run_var_out,
+                      workspace, stream=None, events=None):
+    ws, nbytes = _ws(workspace)
+    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(gamma), _ptr(beta), _ptr(run_mean_in), _ptr(run_var_in),
+            float(eps), float(momentum), _ptr(z), _ptr(y), _ptr(relu_mask), _ptr(saved_mean),
+            _ptr(saved_invstd), _ptr(run_mean_out), _ptr(run_var_out), ws, nbytes, _stream(stream))
+    if events is None:
+        _check(_load().cbr_forward_train(*args), "cbr_forward_train")
+    else:
+        _check(_load().cbr_forward_train_ev(*args, _events(events)), "cbr_forward_train_ev")
+
+
+def cbr_forward_infer(shape, x, w, conv_bias, gamma, beta, run_mean, run_var, eps, y,
+                      workspace, stream=None, events=None):
+    ws, nbytes = _ws(workspace)
+    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(conv_bias), _ptr(gamma), _ptr(beta), _ptr(run_mean),
+            _ptr(run_var), float(eps), _ptr(y), ws, nbytes, _stream(stream))
+    if events is None:
+        _check(_load().cbr_forward_infer(*args), "cbr_forward_infer")
+    else:
+        _check(_load().cbr_forward_infer_ev(*args, _events(events)), "cbr_forward_infer_ev")
+
+
+def cbr_backward(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd,
+                 dz, dgamma, dbeta, dw, dx, workspace, stream=None, events=None):
+    ws, nbytes = _ws(workspace)
+    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(z), _ptr(relu_mask), _ptr(dy), _ptr(gamma),
+            _ptr(saved_mean), _ptr(saved_invstd), _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(dw),
+            _ptr(dx), ws, nbytes, _stream(stream))
+    if events is None:
+        _check(_load().cbr_backward(*args), "cbr_backward")
+    else:
+        _check(_load().cbr_backward_ev(*args, _events(events)), "cbr_backward_ev")

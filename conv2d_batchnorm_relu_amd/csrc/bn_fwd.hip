@@ -1,0 +1,233 @@
+// bn_fwd.hip -- batch-norm finalize, normalise + ReLU + packed mask, and the BN fold.
+#include "cbr_launch.h"
+
+namespace cbr {
+namespace {
+
+constexpr int NT = 256;
+
+// Column sums of a [B][2][K] fp32 partial array over B, in fp64 and a fixed order:
+// block b covers rows [b*bpb, (b+1)*bpb); when K <= 256 the threads split into 256/K
+// subgroups striding over the rows, combined in subgroup order.
+__global__ __launch_bounds__(NT) void colsum_stage1_kernel(const float *__restrict__ part, int B, int K, int bpb,
+                                                           double *__restrict__ pp)
+{
+    __shared__ double red[2][NT];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int t0 = b * bpb, t1 = min(B, t0 + bpb);
+    if (K <= NT) {
+        const int nsub = NT / K;
+        const int k = tid % K, sub = tid / K;
+        double s1 = 0.0, s2 = 0.0;
+        if (sub < nsub)
+            for (int t = t0 + sub; t < t1; t += nsub) {
+                s1 += part[(size_t)t * 2 * K + k];
+                s2 += part[(size_t)t * 2 * K + K + k];
+            }
+        red[0][tid] = s1;
+        red[1][tid] = s2;
+        __syncthreads();
+        if (tid < K) {
+            double a = 0.0, c = 0.0;
+            for (int s = 0; s < nsub; ++s) {
+                a += red[0][s * K + tid];
+                c += red[1][s * K + tid];
+            }
+            pp[(size_t)b * 2 * K + tid] = a;
+            pp[(size_t)b * 2 * K + K + tid] = c;
+        }
+    } else {
+        for (int k = tid; k < K; k += NT) {
+            double s1 = 0.0, s2 = 0.0;
+            for (int t = t0; t < t1; ++t) {
+                s1 += part[(size_t)t * 2 * K + k];
+                s2 += part[(size_t)t * 2 * K + K + k];
+            }
+            pp[(size_t)b * 2 * K + k] = s1;
+            pp[(size_t)b * 2 * K + K + k] = s2;
+        }
+    }
+}
+
+// Stage 2: the BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per
+// channel: mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the
+// difference accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
+// eq_bias = beta - gamma*mean*inv_std, and the running update
+// next = (1 - momentum)*prev + momentum*batch (BatchNorm CUDA page, section 2.4).
+// rm_out/rv_out may alias rm_in/rv_in: each thread reads its channel before writing it.
+__global__ __launch_bounds__(NT) void stats_finalize_kernel(const double *__restrict__ pp, int G, int K,
+                                                            double M, const float *__restrict__ gamma,
+                                                            const float *__restrict__ beta, const float *rm_in,
+                                                            const float *rv_in, float eps, float momentum,
+                                                            float *__restrict__ scale, float *__restrict__ shift,
+                                                            float *__restrict__ saved_mean,
+                                                            float *__restrict__ saved_invstd, float *rm_out,
+                                                            float *rv_out)
+{
+    for (int k = blockIdx.x * NT + threadIdx.x; k < K; k += gridDim.x * NT) {
+        double s1 = 0.0, s2 = 0.0;
+        for (int b = 0; b < G; ++b) {
+            s1 += pp[(size_t)b * 2 * K + k];
+            s2 += pp[(size_t)b * 2 * K + K + k];
+        }
+        const double mean = s1 / M;
+        double var = s2 / M - mean * mean;
+        if (!(var > 0.0)) var = 0.0;
+        const double invstd = 1.0 / sqrt(var + (double)eps);
+        const double gm = (double)gamma[k];
+        scale[k] = (float)(gm * invstd);
+        shift[k] = (float)((double)beta[k] - gm * mean * invstd);
+        saved_mean[k] = (float)mean;
+        saved_invstd[k] = (float)invstd;
+        const double mo = (double)momentum;
+        const float rm = rm_in[k], rv = rv_in[k];
+        rm_out[k] = (float)((1.0 - mo) * (double)rm + mo * mean);
+        rv_out[k] = (float)((1.0 - mo) * (double)rv + mo * var);
+    }
+}
+
+// Normalise + ReLU + mask (CBR page, section 4.3): u = z*eq_scale + eq_bias, y = max(u, 0),
+// mask bit = (u > 0), one pass over z.  Each thread handles UNROLL 16-byte chunks of
+// eight channels; chunk c covers elements 8c..8c+7 of the NHWC linear order, so its
+// eight mask bits are byte c of the little-endian packed mask.  With FIXEDK the chunk's
+// channel group is the same for every chunk a thread visits (256 % (K/8) == 0), so the
+// per-channel coefficients are loaded once.
+constexpr int APPLY_UNROLL = 4;
+
+template <bool FIXEDK>
+__global__ __launch_bounds__(NT) void bn_apply_relu_mask_kernel(const u32x4 *__restrict__ z,
+                                                                const float *__restrict__ scale,
+                                                                const float *__restrict__ shift,
+                                                                u32x4 *__restrict__ y,
+                                                                uint8_t *__restrict__ mask, int chunks, int cpr)
+{
+    const int base = blockIdx.x * NT * APPLY_UNROLL + threadIdx.x;
+    float sc[8], sf[8];
+    if constexpr (FIXEDK) {
+        const int k0 = (threadIdx.x % cpr) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sc[e] = scale[k0 + e];
+            sf[e] = shift[k0 + e];
+        }
+    }
+    u32x4 v[APPLY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < APPLY_UNROLL; ++u) {
+        const int c = base + u * NT;
+        v[u] = c < chunks ? z[c] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < APPLY_UNROLL; ++u) {
+        const int c = base + u * NT;
+        if (c >= chunks) break;
+        if constexpr (!FIXEDK) {
+            const int k0 = (c % cpr) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sc[e] = scale[k0 + e];
+                sf[e] = shift[k0 + e];
+            }
+        }
+        uint32_t bits = 0;
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float u0 = fmaf(bf16_lo(v[u][h]), sc[2 * h], sf[2 * h]);
+            const float u1 = fmaf(bf16_hi(v[u][h]), sc[2 * h + 1], sf[2 * h + 1]);
+            const bool p0 = u0 > 0.f, p1 = u1 > 0.f;
+            bits |= (uint32_t)p0 << (2 * h);
+            bits |= (uint32_t)p1 << (2 * h + 1);
+            o[h] = pack_bf16x2(p0 ? u0 : 0.f, p1 ? u1 : 0.f);
+        }
+        y[c] = u32x4{o[0], o[1], o[2], o[3]};
+        mask[c] = (uint8_t)bits;
+        if (c == chunks - 1)   // zero the unused bytes of the last mask word
+            for (int t = chunks; t < ((chunks + 3) & ~3); ++t) mask[t] = 0;
+    }
+}
+
+// The BN fold (CBR page, section 2; BatchNorm CUDA page, section 4.4):
+// s_k = gamma_k / sqrt(run_var_k + eps), w_fold = bf16(w * s_k),
+// b_fold_k = (b_k - run_mean_k) * s_k + beta_k.
+__global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict__ w, const float *__restrict__ bias,
+                                                     const float *__restrict__ gamma, const float *__restrict__ beta,
+                                                     const float *__restrict__ rm, const float *__restrict__ rv,
+                                                     float eps, int K, int Kg, uint16_t *__restrict__ wf,
+                                                     float *__restrict__ bf)
+{
+    const long total = (long)K * Kg;
+    for (long i = (long)blockIdx.x * NT + threadIdx.x; i < total; i += (long)gridDim.x * NT) {
+        const int k = (int)(i / Kg);
+        const double sd = (double)gamma[k] / sqrt((double)rv[k] + (double)eps);
+        wf[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(w[i]) * (float)sd);
+        if (i < K) {
+            const int kb = (int)i;
+            const double s2 = (double)gamma[kb] / sqrt((double)rv[kb] + (double)eps);
+            const double b = bias ? (double)bias[kb] : 0.0;
+            bf[kb] = (float)((b - (double)rm[kb]) * s2 + (double)beta[kb]);
+        }
+    }
+}
+
+}  // namespace
+
+static int colsum_rows_per_group(int B)
+{
+    const int G = std::min(COLSUM_MAX_GROUPS, B);
+    return (B + G - 1) / G;
+}
+
+int colsum_groups(int B)
+{
+    const int bpb = colsum_rows_per_group(B);
+    return (B + bpb - 1) / bpb;
+}
+
+hipError_t launch_colsum(const float *part, int B, int K, double *pp, hipStream_t st)
+{
+    const int bpb = colsum_rows_per_group(B);
+    colsum_stage1_kernel<<<colsum_groups(B), NT, 0, st>>>(part, B, K, bpb, pp);
+    return hipGetLastError();
+}
+
+hipError_t launch_stats_finalize(int tiles_m, int K, long M, const float *partials, double *pp,
+                                 const float *gamma, const float *beta, const float *rm_in,
+                                 const float *rv_in, float eps, float momentum, float *scale,
+                                 float *shift, float *saved_mean, float *saved_invstd,
+                                 float *rm_out, float *rv_out, hipStream_t st)
+{
+    hipError_t e = launch_colsum(partials, tiles_m, K, pp, st);
+    if (e != hipSuccess) return e;
+    stats_finalize_kernel<<<(K + NT - 1) / NT, NT, 0, st>>>(pp, colsum_groups(tiles_m), K, (double)M, gamma, beta,
+                                                            rm_in, rv_in, eps, momentum, scale, shift, saved_mean,
+                                                            saved_invstd, rm_out, rv_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,
+                                     const float *shift, uint16_t *y, uint8_t *mask, hipStream_t st)
+{
+    const int chunks = (int)(M * K / 8);
+    const int cpr = K / 8;
+    const int blocks = (chunks + NT * APPLY_UNROLL - 1) / (NT * APPLY_UNROLL);
+    if (NT % cpr == 0)
+        bn_apply_relu_mask_kernel<true><<<blocks, NT, 0, st>>>((const u32x4 *)z, scale, shift, (u32x4 *)y,
+                                                               mask, chunks, cpr);
+    else
+        bn_apply_relu_mask_kernel<false><<<blocks, NT, 0, st>>>((const u32x4 *)z, scale, shift, (u32x4 *)y,
+                                                                mask, chunks, cpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, const float *gamma,
+                          const float *beta, const float *rm, const float *rv, float eps,
+                          uint16_t *w_fold, float *b_fold, hipStream_t st)
+{
+    const long total = (long)K * Kg;
+    const int blocks = (int)std::min<long>((total + NT - 1) / NT, 4096);
+    bn_fold_kernel<<<blocks, NT, 0, st>>>(w, bias, gamma, beta, rm, rv, eps, K, Kg, w_fold, b_fold);
+    return hipGetLastError();
+}
+
+}  // namespace cbr

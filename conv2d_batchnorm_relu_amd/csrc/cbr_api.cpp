@@ -1,0 +1,303 @@
+// cbr_api.cpp -- the C ABI of libcbr.so: argument validation, workspace layout and the
+// kernel sequence of each call.  Everything here runs on the host; validation finishes
+// before the first HIP call, so a rejected call touches no device state.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/cbr.h"
+#include "cbr_launch.h"
+
+using namespace cbr;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Validates a shape and fills the forward-convolution geometry.
+int make_geom(const cbr_shape *s, ConvGeom *g)
+{
+    if (!s) return CBR_E_NULL;
+    if (s->n <= 0 || s->h <= 0 || s->w <= 0 || s->c <= 0 || s->k <= 0 || s->r <= 0 || s->s <= 0 ||
+        s->stride_h < 1 || s->stride_w < 1 || s->pad_h < 0 || s->pad_w < 0)
+        return CBR_E_SHAPE;
+    const long hp = (long)s->h + 2L * s->pad_h - s->r, wp = (long)s->w + 2L * s->pad_w - s->s;
+    if (hp < 0 || wp < 0) return CBR_E_SHAPE;
+    const long P = hp / s->stride_h + 1, Q = wp / s->stride_w + 1;
+    if (s->k % 8 != 0 || s->k > 2048) return CBR_E_UNSUPPORTED;
+    if (s->pad_h >= s->r || s->pad_w >= s->s) return CBR_E_UNSUPPORTED;
+    const double lim = 2147483647.0;
+    if ((double)s->n * s->h * s->w * s->c > lim || (double)s->k * s->r * s->s * s->c > lim ||
+        (double)s->n * P * Q * s->k > lim)
+        return CBR_E_UNSUPPORTED;
+    g->N = s->n; g->H = s->h; g->W = s->w; g->C = s->c;
+    g->K = s->k; g->R = s->r; g->S = s->s;
+    g->sh = s->stride_h; g->sw = s->stride_w; g->ph = s->pad_h; g->pw = s->pad_w;
+    g->P = (int)P; g->Q = (int)Q;
+    g->M = (int)(s->n * P * Q);
+    g->Kg = s->r * s->s * s->c;
+    return CBR_OK;
+}
+
+// The data gradient as a stride-1 forward convolution of dz with the flipped filter.
+ConvGeom dgrad_geom(const ConvGeom &g)
+{
+    ConvGeom d;
+    d.N = g.N; d.H = g.P; d.W = g.Q; d.C = g.K;
+    d.K = g.C; d.R = g.R; d.S = g.S;
+    d.sh = 1; d.sw = 1; d.ph = g.R - 1 - g.ph; d.pw = g.S - 1 - g.pw;
+    d.P = g.H; d.Q = g.W;
+    d.M = g.N * g.H * g.W;
+    d.Kg = g.R * g.S * g.K;
+    return d;
+}
+
+struct TrainLayout { size_t partials, pp, scale, shift, total; };
+struct InferLayout { size_t wfold, bfold, total; };
+struct BwdLayout { size_t dz, part, pp, coef, wpart, wflip, total; };
+
+TrainLayout train_layout(const ConvGeom &g)
+{
+    const ConvPlan p = conv_plan(g);
+    TrainLayout L;
+    size_t o = 0;
+    L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)p.tiles_m);
+    L.pp = o; o = align_up(o + sizeof(double) * 2 * g.K * (size_t)COLSUM_MAX_GROUPS);
+    L.scale = o; o = align_up(o + sizeof(float) * g.K);
+    L.shift = o; o = align_up(o + sizeof(float) * g.K);
+    L.total = o;
+    return L;
+}
+
+InferLayout infer_layout(const ConvGeom &g)
+{
+    InferLayout L;
+    size_t o = 0;
+    L.wfold = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.K * g.Kg);
+    L.bfold = o; o = align_up(o + sizeof(float) * g.K);
+    L.total = o;
+    return L;
+}
+
+BwdLayout bwd_layout(const ConvGeom &g)
+{
+    BwdLayout L;
+    const WgradPlan wp = wgrad_plan(g.M, g.K, g.Kg);
+    size_t o = 0;
+    L.dz = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.M * g.K);
+    L.part = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)bnbwd_blocks(g.M, g.K));
+    L.pp = o; o = align_up(o + sizeof(double) * 2 * g.K * (size_t)COLSUM_MAX_GROUPS);
+    L.coef = o; o = align_up(o + sizeof(float) * 3 * g.K);
+    L.wpart = o; o = align_up(o + (wp.splits > 1 ? sizeof(float) * (size_t)wp.splits * g.K * g.Kg : 0));
+    L.wflip = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.K * g.Kg);
+    L.total = o;
+    return L;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename... T>
+bool all_aligned(T... ps) { return (aligned16(ps) && ...); }
+
+template <typename... T>
+bool any_null(T... ps) { return ((ps == nullptr) || ...); }
+
+char *ws_at(void *ws, size_t off) { return (char *)ws + off; }
+
+// Records events[i] on the stream when profiling events were supplied.
+bool mark(void *const *events, int i, hipStream_t s)
+{
+    return !events || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *cbr_status_str(int status)
+{
+    switch (status) {
+    case CBR_OK: return "CBR_OK";
+    case CBR_E_NULL: return "CBR_E_NULL: a required pointer is NULL";
+    case CBR_E_SHAPE: return "CBR_E_SHAPE: invalid shape (sizes, stride, padding, empty output, or one output pixel in training)";
+    case CBR_E_UNSUPPORTED: return "CBR_E_UNSUPPORTED: shape outside the supported limits";
+    case CBR_E_ALIGN: return "CBR_E_ALIGN: a tensor pointer is not 16-byte aligned";
+    case CBR_E_WORKSPACE: return "CBR_E_WORKSPACE: workspace missing or too small";
+    case CBR_E_HIP: return "CBR_E_HIP: a kernel launch failed";
+    case CBR_E_VALUE: return "CBR_E_VALUE: eps or momentum out of range";
+    default: return "CBR: unknown status";
+    }
+}
+
+int cbr_output_hw(const cbr_shape *shape, int32_t *p, int32_t *q)
+{
+    ConvGeom g;
+    const int st = make_geom(shape, &g);
+    if (st != CBR_OK) return st;
+    if (p) *p = g.P;
+    if (q) *q = g.Q;
+    return CBR_OK;
+}
+
+size_t cbr_mask_words(const cbr_shape *shape)
+{
+    ConvGeom g;
+    if (make_geom(shape, &g) != CBR_OK) return 0;
+    return ((size_t)g.M * g.K + 31) / 32;
+}
+
+size_t cbr_workspace_bytes(const cbr_shape *shape, int op)
+{
+    ConvGeom g;
+    if (make_geom(shape, &g) != CBR_OK) return 0;
+    switch (op) {
+    case CBR_OP_TRAIN: return train_layout(g).total;
+    case CBR_OP_INFER: return infer_layout(g).total;
+    case CBR_OP_BWD: return bwd_layout(g).total;
+    default: return 0;
+    }
+}
+
+int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *gamma,
+                         const float *beta, const float *run_mean_in, const float *run_var_in, float eps,
+                         float momentum, uint16_t *z, uint16_t *y, uint32_t *relu_mask, float *saved_mean,
+                         float *saved_invstd, float *run_mean_out, float *run_var_out, void *workspace,
+                         size_t ws_bytes, void *stream, void *const *events)
+{
+    ConvGeom g;
+    int st = make_geom(shape, &g);
+    if (st != CBR_OK) return st;
+    if (any_null(x, w, gamma, beta, run_mean_in, run_var_in, z, y, relu_mask, saved_mean, saved_invstd,
+                 run_mean_out, run_var_out))
+        return CBR_E_NULL;
+    if (!all_aligned(x, w, gamma, beta, run_mean_in, run_var_in, z, y, relu_mask, saved_mean, saved_invstd,
+                     run_mean_out, run_var_out))
+        return CBR_E_ALIGN;
+    if (g.M < 2) return CBR_E_SHAPE;   // batch statistics need two values per channel
+    if (!(eps >= 0.f) || !isfinite(eps) || !(momentum >= 0.f && momentum <= 1.f)) return CBR_E_VALUE;
+    const TrainLayout L = train_layout(g);
+    if (!workspace || ws_bytes < L.total) return CBR_E_WORKSPACE;
+    if (!aligned16(workspace)) return CBR_E_ALIGN;
+
+    hipStream_t s = (hipStream_t)stream;
+    float *partials = (float *)ws_at(workspace, L.partials);
+    double *pp = (double *)ws_at(workspace, L.pp);
+    float *scale = (float *)ws_at(workspace, L.scale);
+    float *shift = (float *)ws_at(workspace, L.shift);
+    const ConvPlan p = conv_plan(g);
+    // conv + per-tile channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
+    if (!mark(events, 0, s)) return CBR_E_HIP;
+    if (launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s) != hipSuccess) return CBR_E_HIP;
+    if (!mark(events, 1, s)) return CBR_E_HIP;
+    if (launch_stats_finalize(p.tiles_m, g.K, g.M, partials, pp, gamma, beta, run_mean_in, run_var_in, eps,
+                              momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out,
+                              s) != hipSuccess)
+        return CBR_E_HIP;
+    if (!mark(events, 2, s)) return CBR_E_HIP;
+    if (launch_bn_apply_relu_mask(g.M, g.K, z, scale, shift, y, (uint8_t *)relu_mask, s) != hipSuccess)
+        return CBR_E_HIP;
+    if (!mark(events, 3, s)) return CBR_E_HIP;
+    return CBR_OK;
+}
+
+int cbr_forward_train(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *gamma,
+                      const float *beta, const float *run_mean_in, const float *run_var_in, float eps,
+                      float momentum, uint16_t *z, uint16_t *y, uint32_t *relu_mask, float *saved_mean,
+                      float *saved_invstd, float *run_mean_out, float *run_var_out, void *workspace,
+                      size_t ws_bytes, void *stream)
+{
+    return cbr_forward_train_ev(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, momentum, z, y,
+                                relu_mask, saved_mean, saved_invstd, run_mean_out, run_var_out, workspace,
+                                ws_bytes, stream, nullptr);
+}
+
+int cbr_forward_infer_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *conv_bias,
+                         const float *gamma, const float *beta, const float *run_mean, const float *run_var,
+                         float eps, uint16_t *y, void *workspace, size_t ws_bytes, void *stream,
+                         void *const *events)
+{
+    ConvGeom g;
+    int st = make_geom(shape, &g);
+    if (st != CBR_OK) return st;
+    if (any_null(x, w, gamma, beta, run_mean, run_var, y)) return CBR_E_NULL;
+    if (!all_aligned(x, w, gamma, beta, run_mean, run_var, y) || (conv_bias && !aligned16(conv_bias)))
+        return CBR_E_ALIGN;
+    if (!(eps >= 0.f) || !isfinite(eps)) return CBR_E_VALUE;
+    const InferLayout L = infer_layout(g);
+    if (!workspace || ws_bytes < L.total) return CBR_E_WORKSPACE;
+    if (!aligned16(workspace)) return CBR_E_ALIGN;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t *wf = (uint16_t *)ws_at(workspace, L.wfold);
+    float *bf = (float *)ws_at(workspace, L.bfold);
+    if (!mark(events, 0, s)) return CBR_E_HIP;
+    if (launch_bn_fold(g.K, g.Kg, w, conv_bias, gamma, beta, run_mean, run_var, eps, wf, bf, s) != hipSuccess)
+        return CBR_E_HIP;
+    if (!mark(events, 1, s)) return CBR_E_HIP;
+    if (launch_conv_fprop(g, EPI_BIAS_RELU, x, wf, bf, y, nullptr, s) != hipSuccess) return CBR_E_HIP;
+    if (!mark(events, 2, s)) return CBR_E_HIP;
+    return CBR_OK;
+}
+
+int cbr_forward_infer(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *conv_bias,
+                      const float *gamma, const float *beta, const float *run_mean, const float *run_var,
+                      float eps, uint16_t *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    return cbr_forward_infer_ev(shape, x, w, conv_bias, gamma, beta, run_mean, run_var, eps, y, workspace,
+                                ws_bytes, stream, nullptr);
+}
+
+int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const uint16_t *z,
+                    const uint32_t *relu_mask, const uint16_t *dy, const float *gamma, const float *saved_mean,
+                    const float *saved_invstd, uint16_t *dz, float *dgamma, float *dbeta, float *dw,
+                    uint16_t *dx, void *workspace, size_t ws_bytes, void *stream, void *const *events)
+{
+    ConvGeom g;
+    int st = make_geom(shape, &g);
+    if (st != CBR_OK) return st;
+    if (any_null(x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd, dgamma, dbeta, dw)) return CBR_E_NULL;
+    if (!all_aligned(x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd, dgamma, dbeta, dw) ||
+        (dz && !aligned16(dz)) || (dx && !aligned16(dx)))
+        return CBR_E_ALIGN;
+    if (g.M < 2) return CBR_E_SHAPE;
+    if (dx && (g.sh != 1 || g.sw != 1)) return CBR_E_UNSUPPORTED;
+    const BwdLayout L = bwd_layout(g);
+    if (!workspace || ws_bytes < L.total) return CBR_E_WORKSPACE;
+    if (!aligned16(workspace)) return CBR_E_ALIGN;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t *dzp = dz ? dz : (uint16_t *)ws_at(workspace, L.dz);
+    // masked BN backward (CBR page 5.1) -> WGrad -> DGrad (5.2; skipped for the first layer, 5.3).
+    // WGrad is enqueued before DGrad on the same stream, so it has finished reading x
+    // before DGrad may overwrite it when dx aliases x.
+    if (!mark(events, 0, s)) return CBR_E_HIP;
+    if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
+                           (float *)ws_at(workspace, L.part), (double *)ws_at(workspace, L.pp),
+                           (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s) != hipSuccess)
+        return CBR_E_HIP;
+    if (!mark(events, 1, s)) return CBR_E_HIP;
+    if (launch_conv_wgrad(g, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s) != hipSuccess) return CBR_E_HIP;
+    if (!mark(events, 2, s)) return CBR_E_HIP;
+    if (dx) {
+        uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
+        if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s) != hipSuccess) return CBR_E_HIP;
+        const ConvGeom d = dgrad_geom(g);
+        if (launch_conv_fprop(d, EPI_PLAIN, dzp, wt, nullptr, dx, nullptr, s) != hipSuccess) return CBR_E_HIP;
+    }
+    if (!mark(events, 3, s)) return CBR_E_HIP;
+    return CBR_OK;
+}
+
+int cbr_backward(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const uint16_t *z,
+                 const uint32_t *relu_mask, const uint16_t *dy, const float *gamma, const float *saved_mean,
+                 const float *saved_invstd, uint16_t *dz, float *dgamma, float *dbeta, float *dw, uint16_t *dx,
+                 void *workspace, size_t ws_bytes, void *stream)
+{
+    return cbr_backward_ev(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd, dz, dgamma, dbeta, dw,
+                           dx, workspace, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -74,9 +74,13 @@ WORKLOADS = {
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    u = a.view(np.uint32)
+    # finite inputs: u + 0x8000 cannot wrap past 2^32
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -1,0 +1,194 @@
+/*
+ * cbr.h -- C ABI of libcbr.so: the fused Conv2D -> BatchNorm -> ReLU (CBR) operator
+ * on AMD Instinct MI355X (gfx950), training forward, folded-BN inference and backward.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [CBR]  Tech-Renaissance blog, "(20) CBR fused operator: Conv + BatchNorm + ReLU"
+ *   [BN]   "CUDA implementation of batch normalization (BatchNorm)" (dpshk.com)
+ *   [TL]   "TileLang operator-fusion case: Conv2D+ReLU"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts ([CBR] section 8): activations NHWC, filters KRSC (K = output channels),
+ * conv outputs N x P x Q x K, all dense.  P = (H + 2*pad_h - R)/stride_h + 1 and
+ * Q = (W + 2*pad_w - S)/stride_w + 1 (floor); the convolution is a cross-correlation
+ * with zero padding, dilation 1, one group.  M = N*P*Q is the number of output pixels.
+ *
+ * Types: tensors marked bf16 are bfloat16 bit patterns (uint16_t); statistics,
+ * gamma/beta, the weight gradient and conv bias are float32.
+ *
+ * Pointers: every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
+ * caller; the library never allocates, frees or keeps device memory.  The cbr_shape
+ * pointer is a host pointer read during the call only.  `workspace` is caller-owned
+ * device scratch of at least cbr_workspace_bytes(shape, op) bytes (256-byte aligned);
+ * its contents are undefined between calls and it must not be shared by calls that
+ * may run concurrently.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Execution: each call validates its arguments on the host, then enqueues its
+ * kernels on `stream` and returns without synchronising.  Faults during kernel
+ * execution surface at the caller's next synchronisation, as HIP reports them.
+ * Results are bitwise reproducible run to run (no floating-point atomics).
+ *
+ * Errors: a non-zero return means nothing was enqueued and no output was written,
+ * except CBR_E_HIP, which reports a failed launch (outputs then undefined).  No call
+ * aborts or exits the process.
+ *
+ * Limits (CBR_E_UNSUPPORTED): K % 8 != 0 ([CBR] section 8: output channels a multiple
+ * of 8); K > 2048; any tensor with 2^31 elements or more; pad >= filter size;
+ * dx requested with a stride other than 1.
+ */
+#ifndef CBR_H
+#define CBR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cbr_shape {
+    int32_t n, h, w, c;                     /* input, NHWC                         */
+    int32_t k, r, s;                        /* filter, KRSC (k = output channels)  */
+    int32_t stride_h, stride_w, pad_h, pad_w;
+} cbr_shape;
+
+enum cbr_status {
+    CBR_OK = 0,
+    CBR_E_NULL = 1,         /* a required pointer is NULL                            */
+    CBR_E_SHAPE = 2,        /* non-positive size, stride < 1, negative pad, empty out,
+                               or M < 2 in training (no batch variance from one value) */
+    CBR_E_UNSUPPORTED = 3,  /* valid but outside the limits listed above             */
+    CBR_E_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned               */
+    CBR_E_WORKSPACE = 5,    /* workspace NULL or smaller than cbr_workspace_bytes    */
+    CBR_E_HIP = 6,          /* a kernel launch failed                                */
+    CBR_E_VALUE = 7         /* eps < 0, momentum outside [0,1], or not finite        */
+};
+
+enum cbr_op { CBR_OP_TRAIN = 0, CBR_OP_INFER = 1, CBR_OP_BWD = 2 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *cbr_status_str(int status);
+
+/* Checks the shape alone; writes P and Q when they are non-NULL.  Returns a status. */
+int cbr_output_hw(const cbr_shape *shape, int32_t *p, int32_t *q);
+
+/* Number of uint32 words of the packed ReLU mask: ceil(M*K / 32). */
+size_t cbr_mask_words(const cbr_shape *shape);
+
+/* Workspace bytes that op (enum cbr_op) needs for this shape; 0 for an invalid shape.
+ * For CBR_OP_BWD the figure includes room for dz, used when the caller passes dz = NULL. */
+size_t cbr_workspace_bytes(const cbr_shape *shape, int op);
+
+/*
+ * Training-mode forward ([CBR] sections 2 and 4.1-4.3; [BN] 2.1, 2.4):
+ *   z        = conv(x, w)                                   bf16 [N,P,Q,K]  (out)
+ *   mean_k   = (1/M) sum z,  var_k = (1/M) sum (z - mean_k)^2   (biased; from the
+ *              fp32 accumulators, before z is rounded to bf16)
+ *   invstd_k = 1/sqrt(var_k + eps)
+ *   u        = gamma_k * (z - mean_k) * invstd_k + beta_k  (computed from stored z)
+ *   y        = max(u, 0)                                    bf16 [N,P,Q,K]  (out)
+ *   relu_mask: bit (i % 32) of word (i / 32) is (u_i > 0) for the NHWC linear index i
+ *              of y; cbr_mask_words() words, bits past M*K are zero        (out)
+ *   saved_mean = mean, saved_invstd = invstd                   float [K]   (out)
+ *   run_mean_out = (1-momentum)*run_mean_in + momentum*mean    float [K]   (out)
+ *   run_var_out  = (1-momentum)*run_var_in  + momentum*var     float [K]   (out)
+ * x: bf16 NHWC [N,H,W,C]; w: bf16 KRSC [K,R,S,C]; gamma, beta, run_*_in: float [K].
+ * Needs M >= 2 (CBR_E_SHAPE otherwise).  u normalises the stored bf16 z with statistics
+ * of the unrounded values, so a channel whose batch variance is below the bf16 rounding
+ * error of its values (var << (2^-8 |z|)^2, e.g. a constant non-zero channel) gets u
+ * dominated by that rounding error.
+ * run_mean_out/run_var_out may alias run_mean_in/run_var_in (in-place update); no other
+ * output may alias an input.  There is no conv bias: batch normalisation cancels it.
+ */
+int cbr_forward_train(const cbr_shape *shape,
+                      const uint16_t *x, const uint16_t *w,
+                      const float *gamma, const float *beta,
+                      const float *run_mean_in, const float *run_var_in,
+                      float eps, float momentum,
+                      uint16_t *z, uint16_t *y, uint32_t *relu_mask,
+                      float *saved_mean, float *saved_invstd,
+                      float *run_mean_out, float *run_var_out,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Folded-BN inference forward ([CBR] sections 2 and 6; [BN] 4.4; [TL] fused ReLU
+ * epilogue):
+ *   s_k      = gamma_k / sqrt(run_var_k + eps)
+ *   w_fold   = w * s_k (per output channel, rounded to bf16),
+ *   b_fold_k = (b_k - run_mean_k) * s_k + beta_k   (float)
+ *   y        = max(conv(x, w_fold) + b_fold, 0)                   bf16 [N,P,Q,K] (out)
+ * conv_bias may be NULL (read as zero).  All other pointers as in training.
+ */
+int cbr_forward_infer(const cbr_shape *shape,
+                      const uint16_t *x, const uint16_t *w, const float *conv_bias,
+                      const float *gamma, const float *beta,
+                      const float *run_mean, const float *run_var, float eps,
+                      uint16_t *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the training forward ([CBR] section 5; [BN] 3.1-3.3):
+ *   g      = dy * mask                      (never written to memory)
+ *   xhat   = (z - saved_mean) * saved_invstd (recomputed from the stored bf16 z)
+ *   dbeta  = sum_m g,  dgamma = sum_m g * xhat                       float [K] (out)
+ *   dz     = gamma * saved_invstd * (g - dbeta/M - xhat * dgamma/M)  bf16 [N,P,Q,K]
+ *   dw[k,r,s,c] = sum_{n,p,q} dz[n,p,q,k] * x[n, p*sh-ph+r, q*sw-pw+s, c]  float KRSC
+ *   dx[n,h,v,c] = sum_{k,r,s} dz[n,p,q,k] * w[k,r,s,c] over the (p,q) that read
+ *                 x[n,h,v] through tap (r,s)                           bf16 NHWC
+ *   dw and dx are computed from the bf16 dz above (as the CBR page's WGrad and DGrad
+ *   read dL/d(conv_out) from a half-precision buffer), accumulated in fp32.
+ * Needs M >= 2 (CBR_E_SHAPE otherwise).
+ * Inputs: x, w, z (bf16), relu_mask, dy (bf16 [N,P,Q,K]), gamma, saved_mean,
+ * saved_invstd (float [K]) -- the training forward's inputs and outputs.
+ * dz may be NULL (then it lives in the workspace).  dx may be NULL: the first-layer
+ * form of [CBR] 5.3, which skips the data gradient.  dx may alias x: the weight
+ * gradient finishes reading x before the data gradient writes dx ([CBR] 5.2).
+ * A non-NULL dx needs stride 1 in both directions.
+ */
+int cbr_backward(const cbr_shape *shape,
+                 const uint16_t *x, const uint16_t *w, const uint16_t *z,
+                 const uint32_t *relu_mask, const uint16_t *dy,
+                 const float *gamma, const float *saved_mean, const float *saved_invstd,
+                 uint16_t *dz, float *dgamma, float *dbeta, float *dw, uint16_t *dx,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Timed variants for profiling: identical to the calls above, and in addition record
+ * caller-created hipEvent_t handles (passed as void*) on `stream` around each kernel
+ * stage, so a caller can time the stages with hipEventElapsedTime.  `events` may be
+ * NULL (then the call is exactly the untimed one).  Events recorded:
+ *   train:  [0] before the convolution, [1] after it, [2] after the statistics
+ *           finalize, [3] after normalise + ReLU + mask                 (4 events)
+ *   infer:  [0] before the fold, [1] after it, [2] after the convolution (3 events)
+ *   bwd:    [0] before the BN backward, [1] after it (dz ready), [2] after the weight
+ *           gradient, [3] after the data gradient (== [2] when dx is NULL) (4 events)
+ */
+int cbr_forward_train_ev(const cbr_shape *shape,
+                         const uint16_t *x, const uint16_t *w,
+                         const float *gamma, const float *beta,
+                         const float *run_mean_in, const float *run_var_in,
+                         float eps, float momentum,
+                         uint16_t *z, uint16_t *y, uint32_t *relu_mask,
+                         float *saved_mean, float *saved_invstd,
+                         float *run_mean_out, float *run_var_out,
+                         void *workspace, size_t ws_bytes, void *stream, void *const *events);
+
+int cbr_forward_infer_ev(const cbr_shape *shape,
+                         const uint16_t *x, const uint16_t *w, const float *conv_bias,
+                         const float *gamma, const float *beta,
+                         const float *run_mean, const float *run_var, float eps,
+                         uint16_t *y, void *workspace, size_t ws_bytes, void *stream,
+                         void *const *events);
+
+int cbr_backward_ev(const cbr_shape *shape,
+                    const uint16_t *x, const uint16_t *w, const uint16_t *z,
+                    const uint32_t *relu_mask, const uint16_t *dy,
+                    const float *gamma, const float *saved_mean, const float *saved_invstd,
+                    uint16_t *dz, float *dgamma, float *dbeta, float *dw, uint16_t *dx,
+                    void *workspace, size_t ws_bytes, void *stream, void *const *events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBR_H */

@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI: the library loads, exports every function that
+include/cbr.h declares, and its validation rejects bad arguments before any HIP call.
+Every call here fails validation on purpose (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import conv2d_batchnorm_relu_amd as cbr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cbr.h")
+
+FAKE = 0x100000  # 16-byte-aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cbr.library_path()):
+        pytest.fail("libcbr.so is not built; run __graft_entry__.build()")
+    return cbr._load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cbr_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"cbr_forward_train", "cbr_forward_infer", "cbr_backward", "cbr_workspace_bytes"} <= set(names)
+    raw = ctypes.CDLL(cbr.library_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in cbr.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert cbr.cbr_status_str(s).startswith("CBR")
+    assert "unknown" in cbr.cbr_status_str(99)
+
+
+def shp(**kw):
+    base = dict(n=2, h=8, w=8, c=4, k=8, r=3, s=3, stride=1, pad=1)
+    base.update(kw)
+    return cbr.make_shape(**base)
+
+
+def test_output_hw_and_mask_words(lib):
+    assert cbr.cbr_output_hw(shp()) == (8, 8)
+    assert cbr.cbr_output_hw(shp(n=64, h=224, w=224, c=3, k=64, r=7, s=7, stride=2, pad=3)) == (112, 112)
+    assert cbr.cbr_output_hw(shp(h=7, w=6, r=3, s=3, stride=2, pad=0)) == (3, 2)
+    assert cbr.cbr_mask_words(shp()) == 2 * 8 * 8 * 8 // 32
+    assert cbr.cbr_mask_words(shp(n=1, h=1, w=1, c=8, k=8, r=1, s=1, pad=0)) == 1   # 8 bits -> 1 word
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), 2), (dict(h=-1), 2), (dict(stride=0), 2), (dict(pad=-1), 2),
+    (dict(h=2, r=7, s=7, pad=2), 2),            # filter larger than the padded input
+    (dict(k=12), 3), (dict(k=4096), 3),          # K % 8, K > 2048
+    (dict(pad=3), 3),                            # pad >= filter size
+    (dict(n=70000, h=200, w=200, c=64), 3),      # tensor of 2^31 elements or more
+])
+def test_shape_validation(lib, kw, status):
+    with pytest.raises(cbr.CbrError) as e:
+        cbr.cbr_output_hw(shp(**kw))
+    assert e.value.status == status
+    assert cbr.cbr_workspace_bytes(shp(**kw), cbr.CBR_OP_TRAIN) == 0
+
+
+def test_workspace_sizes_positive_and_monotone(lib):
+    small = cbr.cbr_workspace_bytes(shp(), cbr.CBR_OP_TRAIN)
+    big = cbr.cbr_workspace_bytes(shp(n=64), cbr.CBR_OP_TRAIN)
+    assert 0 < small <= big
+    for op in (0, 1, 2):
+        assert cbr.cbr_workspace_bytes(shp(), op) % 256 == 0
+    assert cbr.cbr_workspace_bytes(shp(), 7) == 0
+
+
+def _train(sp, **over):
+    a = dict(x=FAKE, w=FAKE, gamma=FAKE, beta=FAKE, rm=FAKE, rv=FAKE, eps=1e-5, mom=0.1, z=FAKE, y=FAKE,
+             mask=FAKE, sm=FAKE, si=FAKE, rmo=FAKE, rvo=FAKE, ws=FAKE, nbytes=1 << 30)
+    a.update(over)
+    return cbr._load().cbr_forward_train(ctypes.byref(sp), a["x"], a["w"], a["gamma"], a["beta"], a["rm"],
+                                         a["rv"], a["eps"], a["mom"], a["z"], a["y"], a["mask"], a["sm"],
+                                         a["si"], a["rmo"], a["rvo"], a["ws"], a["nbytes"], 0)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(mask=None), 1), (dict(rvo=None), 1),
+    (dict(y=FAKE + 2), 4), (dict(gamma=FAKE + 4), 4),
+    (dict(ws=None), 5), (dict(nbytes=16), 5),
+    (dict(eps=-1.0), 7), (dict(mom=1.5), 7), (dict(eps=float("inf")), 7), (dict(mom=float("nan")), 7),
+])
+def test_train_validation(lib, over, status):
+    assert _train(shp(), **over) == status
+
+
+def test_training_needs_two_output_pixels(lib):
+    one = shp(n=1, h=1, w=1, c=8, k=8, r=1, s=1, pad=0)
+    assert cbr.cbr_output_hw(one) == (1, 1)          # a valid shape ...
+    assert _train(one) == 2                           # ... but no batch variance from one value
+    assert _bwd(one) == 2
+
+
+def test_train_null_shape(lib):
+    st = cbr._load().cbr_forward_train(None, *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 1 << 30, 0)
+    assert st == 1
+
+
+def _bwd(sp, **over):
+    a = dict(x=FAKE, w=FAKE, z=FAKE, mask=FAKE, dy=FAKE, gamma=FAKE, sm=FAKE, si=FAKE, dz=FAKE, dg=FAKE,
+             db=FAKE, dw=FAKE, dx=FAKE, ws=FAKE, nbytes=1 << 30)
+    a.update(over)
+    return cbr._load().cbr_backward(ctypes.byref(sp), a["x"], a["w"], a["z"], a["mask"], a["dy"], a["gamma"],
+                                    a["sm"], a["si"], a["dz"], a["dg"], a["db"], a["dw"], a["dx"], a["ws"],
+                                    a["nbytes"], 0)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dy=None), 1), (dict(dw=None), 1), (dict(dx=FAKE + 8), 4), (dict(dz=FAKE + 8), 4),
+    (dict(nbytes=0), 5),
+])
+def test_backward_validation(lib, over, status):
+    assert _bwd(shp(), **over) == status
+
+
+def test_backward_dx_needs_stride_one(lib):
+    assert _bwd(shp(stride=2)) == 3
+
+
+def _infer(sp, **over):
+    a = dict(x=FAKE, w=FAKE, bias=None, gamma=FAKE, beta=FAKE, rm=FAKE, rv=FAKE, eps=1e-5, y=FAKE, ws=FAKE,
+             nbytes=1 << 30)
+    a.update(over)
+    return cbr._load().cbr_forward_infer(ctypes.byref(sp), a["x"], a["w"], a["bias"], a["gamma"], a["beta"],
+                                         a["rm"], a["rv"], a["eps"], a["y"], a["ws"], a["nbytes"], 0)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(y=None), 1), (dict(bias=FAKE + 4), 4), (dict(ws=FAKE + 8), 4), (dict(nbytes=1), 5),
+    (dict(eps=-0.5), 7),
+])
+def test_infer_validation(lib, over, status):
+    assert _infer(shp(), **over) == status
+
+
+def test_product_never_imports_oracle():
+    """The package and the library sources do not reference the oracle."""
+    pkg = os.path.join(ROOT, "conv2d_batchnorm_relu_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower() or f == "inputs.py", f
+                assert "cbro_" not in text, f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(cbr, "_LIB_PATH", str(tmp_path / "libcbr.so"))
+    monkeypatch.setattr(cbr, "_lib", None)
+    with pytest.raises(ImportError):
+        cbr.cbr_status_str(0)

@@ -1,0 +1,163 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64 oracle on
+the same seeded inputs, element by element (tolerances in tests/cbr_harness.py)."""
+import numpy as np
+import pytest
+
+from conv2d_batchnorm_relu_amd.inputs import Geometry, draw, draw_workload, WORKLOADS
+import cbr_harness as H
+
+pytestmark = pytest.mark.gpu
+
+# Small geometries that still span several tiles and ragged tails (tiles are 128 output
+# pixels x 64 or 128 output channels; K-steps are 64 reduction elements).
+TRAIN_GEOMS = [
+    Geometry(2, 8, 8, 4, 8, 3, 3, 1, 1),         # the tiny workload (C=4: scalar gather path)
+    Geometry(3, 9, 11, 16, 24, 3, 3, 1, 1),      # ragged M (297), K=24 < one channel tile
+    Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1),     # stride 2
+    Geometry(2, 31, 29, 3, 64, 7, 7, 2, 3),      # first-layer form: Cin=3, 7x7, stride 2
+    Geometry(1, 12, 12, 128, 128, 3, 3, 1, 1),   # K=128 tile, Kg=1152
+    Geometry(2, 7, 9, 256, 256, 3, 3, 1, 1),     # two channel tiles
+    Geometry(4, 14, 14, 64, 72, 1, 1, 1, 0),     # 1x1, K=72 (ragged channel tile)
+    Geometry(2, 10, 10, 8, 16, 3, 3, 1, 1),      # C=8: K-steps span several taps
+    Geometry(1, 1, 2, 8, 8, 1, 1, 1, 0),         # two output pixels (the fewest training allows)
+]
+INFER_GEOMS = TRAIN_GEOMS + [Geometry(1, 1, 1, 8, 8, 1, 1, 1, 0)]   # a single output pixel
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import conv2d_batchnorm_relu_amd as cbr
+    cbr._load()
+
+
+@pytest.mark.parametrize("g", TRAIN_GEOMS, ids=str)
+def test_train_forward_small(g):
+    H.log(f"train fwd {g}")
+    d = draw(g, "train", 7)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
+@pytest.mark.parametrize("g", INFER_GEOMS, ids=str)
+def test_infer_small(g):
+    H.log(f"infer {g}")
+    d = draw(g, "infer", 8)
+    y = H.gpu_infer(g, d)
+    ref = H.oracle.forward_infer(H.oshape(g), d["x"], d["w"], d["bias"], d["gamma"], d["beta"],
+                                 d["run_mean"], d["run_var"], 1e-5)
+    H.assert_close(y, ref, "infer y")
+
+
+def test_infer_without_bias():
+    g = Geometry(2, 9, 9, 32, 32, 3, 3, 1, 1)
+    d = draw(g, "infer", 9)
+    d["bias"] = None
+    y = H.gpu_infer(g, d)
+    ref = H.oracle.forward_infer(H.oshape(g), d["x"], d["w"], None, d["gamma"], d["beta"],
+                                 d["run_mean"], d["run_var"], 1e-5)
+    H.assert_close(y, ref, "infer y (no bias)")
+
+
+BWD_GEOMS = [
+    (Geometry(2, 8, 8, 4, 8, 3, 3, 1, 1), True),       # tiny: C=4 dgrad output (scalar stores)
+    (Geometry(3, 9, 11, 16, 24, 3, 3, 1, 1), True),
+    (Geometry(2, 7, 9, 256, 256, 3, 3, 1, 1), True),
+    (Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1), True),
+    (Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1), False),  # stride 2: first-layer form, no dx
+    (Geometry(2, 31, 29, 3, 64, 7, 7, 2, 3), False),   # Cin=3 7x7 s2 weight gradient
+    (Geometry(4, 14, 14, 64, 72, 1, 1, 1, 0), True),
+]
+
+
+@pytest.mark.parametrize("g,want_dx", BWD_GEOMS, ids=str)
+def test_backward_small(g, want_dx):
+    H.log(f"backward {g} dx={want_dx}")
+    d = draw(g, "bwd", 10)
+    res, devt = H.gpu_train(g, d)
+    bw = H.gpu_backward(g, devt, d["dy"], want_dx=want_dx)
+    ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"], want_dx=want_dx)
+    H.check_backward(g, d, bw, ob, want_dx)
+    if not want_dx:
+        assert bw["dx"] is None
+
+
+def test_backward_dz_in_workspace_and_dx_aliasing_x():
+    """dz = NULL keeps dz in the workspace; dx may overwrite x in place."""
+    g = Geometry(2, 12, 12, 32, 32, 3, 3, 1, 1)
+    d = draw(g, "bwd", 11)
+    res, devt = H.gpu_train(g, d)
+    ref = H.gpu_backward(g, devt, d["dy"])
+    alias = H.gpu_backward(g, devt, d["dy"], dz_out=False, dx_alias_x=True)
+    for k in ("dgamma", "dbeta", "dw", "dx"):
+        np.testing.assert_array_equal(alias[k], ref[k], err_msg=k)
+
+
+def test_running_stats_in_place():
+    g = Geometry(2, 9, 9, 16, 16, 3, 3, 1, 1)
+    d = draw(g, "train", 12)
+    d["run_mean"] = np.linspace(-1, 1, g.k).astype(np.float32)
+    d["run_var"] = np.linspace(0.5, 2, g.k).astype(np.float32)
+    res, _ = H.gpu_train(g, d, inplace_running=True)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
+def test_bitwise_deterministic():
+    g = Geometry(8, 20, 20, 64, 64, 3, 3, 1, 1)
+    d = draw(g, "bwd", 13)
+    r1, dv1 = H.gpu_train(g, d)
+    r2, dv2 = H.gpu_train(g, d)
+    for k in ("z", "y", "mask_words", "mean", "invstd", "run_mean", "run_var"):
+        np.testing.assert_array_equal(r1[k], r2[k], err_msg=k)
+    b1 = H.gpu_backward(g, dv1, d["dy"])
+    b2 = H.gpu_backward(g, dv2, d["dy"])
+    for k in b1:
+        np.testing.assert_array_equal(b1[k], b2[k], err_msg=k)
+
+
+# ----------------------------------------------------------------------------------
+# full-size workloads, complete outputs against the complete oracle
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "stem", "s2_train"])
+def test_train_full_workload(name):
+    wl, d = draw_workload(name)
+    g = wl.geom
+    if not wl.bf16:   # the fp32 workload runs on the bf16 path with its values pre-rounded
+        from conv2d_batchnorm_relu_amd.inputs import bf16_round
+        d = {k: (bf16_round(v) if k in ("x", "w", "dy") else v) for k, v in d.items()}
+    H.log(f"full train {name} {g}")
+    res, devt = H.gpu_train(g, d, wl.eps, wl.momentum)
+    H.log("oracle")
+    ora = H.oracle_train(g, d, wl.eps, wl.momentum)
+    flips = H.check_train(g, d, res, ora, wl.eps, wl.momentum)
+    H.log(f"ok, mask flips near zero: {flips}")
+    if name == "tiny":
+        bw = H.gpu_backward(g, devt, d["dy"])
+        ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"])
+        H.check_backward(g, d, bw, ob)
+
+
+def test_infer_full_workload():
+    wl, d = draw_workload("s3_infer")
+    g = wl.geom
+    H.log(f"full infer {g}")
+    y = H.gpu_infer(g, d, wl.eps)
+    ref = H.oracle.forward_infer(H.oshape(g), d["x"], d["w"], d["bias"], d["gamma"], d["beta"],
+                                 d["run_mean"], d["run_var"], wl.eps)
+    H.assert_close(y, ref, "infer y")
+
+
+def test_backward_full_workload():
+    wl, d = draw_workload("s4_bwd")
+    g = wl.geom
+    H.log(f"full backward {g}")
+    res, devt = H.gpu_train(g, d, wl.eps, wl.momentum)
+    bw = H.gpu_backward(g, devt, d["dy"])
+    H.log("oracle")
+    ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"])
+    H.check_backward(g, d, bw, ob)
