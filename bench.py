@@ -130,24 +130,30 @@ def main():
 
     def make_event():
         # torch creates the underlying hipEvent_t on first record; the library then
-        # re-records it on its own stream.
+        # re-records it from its kernels' own dispatch timestamps.
         e = torch.cuda.Event(enable_timing=True)
         e.record()
         return e
 
     def timed(fn, nev, steps, warmup):
-        """Runs fn(events) warmup + steps times; returns (wall ms/step, [per-stage ms])."""
+        """Runs fn warmup times, then `steps` timed calls without events (wall clock,
+        bracketed by device synchronisation), then `steps` calls with per-stage kernel
+        events; returns (ms per call, [mean ms per stage])."""
         for _ in range(warmup):
             fn(None)
-        evs = [[make_event() for _ in range(nev)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for _ in range(steps):
+            fn(None)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        evs = [[make_event() for _ in range(nev)] for _ in range(steps)]
+        torch.cuda.synchronize()
         for i in range(steps):
             fn(evs[i])
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
-        stages = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
-                  for j in range(nev - 1)]
+        stages = [sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(steps)) / steps
+                  for j in range(nev // 2)]
         return wall, stages
 
     # ---------------- headline: training forward ----------------
@@ -170,7 +176,7 @@ def main():
                               rmo, rvo, ws, events=events)
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms, stages = timed(train_step, 4, args.steps, args.warmup)
+    ms, stages = timed(train_step, 6, args.steps, args.warmup)
     flops = conv_flops(g)
     kb = train_bytes(g)
     kernels = [kernel_entry("conv_fprop_stats", stages[0], kb["conv_fprop_stats"], flops),
@@ -185,12 +191,13 @@ def main():
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         for _ in range(args.cold):
             flush.fill_(1)
-            ev = [make_event() for _ in range(4)]
+            ev = [make_event() for _ in range(6)]
+            torch.cuda.synchronize()
             train_step(ev)
             torch.cuda.synchronize()
-            cold.append([ev[j].elapsed_time(ev[j + 1]) for j in range(3)])
+            cold.append(ev[0].elapsed_time(ev[5]))   # first kernel's start to last kernel's end
         del flush
-    cold_ms = float(np.median([sum(c) for c in cold])) if cold else None
+    cold_ms = float(np.median(cold)) if cold else None
 
     out = {
         "metric": "CBR train-fwd TFLOP/s + HBM GB/s (% roofline), N256 56x56 64->64 3x3 bf16",
@@ -236,7 +243,7 @@ def main():
             cbr.cbr_forward_infer(sp4, t4["x"], t4["w"], t4["b"], t4["ga"], t4["be"], t4["rm"], t4["rv"],
                                   wl4.eps, t4["y"], t4["ws"], events=events)
 
-        ms4, st4 = timed(infer_step, 3, steps, 5)
+        ms4, st4 = timed(infer_step, 4, steps, 5)
         ib = infer_bytes(g4)
         aux["infer"] = {"workload": "infer N256 28x28 C128->K128 3x3 s1 p1 (conv bias)", "ms": round(ms4, 5),
                         "tflops": round(conv_flops(g4) / (ms4 * 1e-3) / 1e12, 2),
@@ -272,7 +279,7 @@ def main():
             cbr.cbr_backward(sp5, t5["x"], t5["w"], zz, mk, t5["dy"], t5["ga"], s5m, s5i, dz, dgam, dbet, dw,
                              dx, ws5, events=events)
 
-        ms5, st5 = timed(bwd_step, 4, steps, 5)
+        ms5, st5 = timed(bwd_step, 6, steps, 5)
         bb = bwd_bytes(g5)
         f5 = conv_flops(g5)
         aux["backward"] = {"workload": "backward N256 14x14 C256->K256 3x3 s1 p1", "ms": round(ms5, 5),
@@ -280,7 +287,7 @@ def main():
                            "kernels": [kernel_entry("bn_backward", st5[0], bb["bn_backward"], 0),
                                        kernel_entry("conv_wgrad", st5[1], bb["conv_wgrad"], f5),
                                        kernel_entry("conv_dgrad", st5[2], bb["conv_dgrad"], f5)]}
-        ms5f, st5f = timed(fwd5, 4, steps, 5)
+        ms5f, st5f = timed(fwd5, 6, steps, 5)
         aux["train_s4"] = {"workload": "train forward N256 14x14 C256->K256 3x3", "ms": round(ms5f, 5),
                            "tflops": round(f5 / (ms5f * 1e-3) / 1e12, 2)}
         del t5, zz, yy, mk, ws5, dz, dx
@@ -301,7 +308,7 @@ def main():
             cbr.cbr_forward_train(sp2, t2["x"], t2["w"], t2["ga"], t2["be"], t2["rm"], t2["rv"], wl2.eps,
                                   wl2.momentum, z2, y2, m2, v2[0], v2[1], v2[2], v2[3], ws2, events=events)
 
-        ms2, st2 = timed(stem_step, 4, steps, 5)
+        ms2, st2 = timed(stem_step, 6, steps, 5)
         kb2 = train_bytes(g2)
         aux["stem_train"] = {"workload": "train forward N64 224x224 C3->K64 7x7 s2 p3", "ms": round(ms2, 5),
                              "gbps": round(sum(kb2.values()) / (ms2 * 1e-3) / 1e9, 1),

@@ -6,6 +6,7 @@
 //   apply:    dz = gamma*invstd*(g - dbeta/M - xhat*dgamma/M), written as bf16.
 // g is never written to memory.
 #include "cbr_launch.h"
+#include "cbr_reduce.h"
 
 namespace cbr {
 namespace {
@@ -78,20 +79,20 @@ __global__ __launch_bounds__(NT) void bnbwd_reduce_kernel(const u32x4 *__restric
     }
 }
 
-// dbeta = s1, dgamma = s2; coefficients of the apply step:
-// coef[0] = gamma*invstd, coef[1] = dbeta/M, coef[2] = dgamma/M.
-__global__ __launch_bounds__(NT) void bnbwd_finalize_kernel(const double *__restrict__ pp, int G, int K, double M,
+// dbeta = s1, dgamma = s2 (fp64 over the partial rows, fixed order); coefficients of
+// the apply step: coef[0] = gamma*invstd, coef[1] = dbeta/M, coef[2] = dgamma/M.
+template <typename TIn>
+__global__ __launch_bounds__(NT) void bnbwd_finalize_kernel(const TIn *__restrict__ rows, int R, int K, double M,
                                                             const float *__restrict__ gamma,
                                                             const float *__restrict__ invstd,
                                                             float *__restrict__ coef, float *__restrict__ dgamma,
                                                             float *__restrict__ dbeta)
 {
-    for (int k = blockIdx.x * NT + threadIdx.x; k < K; k += gridDim.x * NT) {
-        double s1 = 0.0, s2 = 0.0;
-        for (int b = 0; b < G; ++b) {
-            s1 += pp[(size_t)b * 2 * K + k];
-            s2 += pp[(size_t)b * 2 * K + K + k];
-        }
+    __shared__ double tot[2 * 2048];
+    __shared__ double scratch[NT * 4];
+    sum_rows_to_lds<TIn>(rows, R, 2 * K, tot, scratch);
+    for (int k = threadIdx.x; k < K; k += NT) {
+        const double s1 = tot[k], s2 = tot[K + k];
         dbeta[k] = (float)s1;
         dgamma[k] = (float)s2;
         coef[k] = gamma[k] * invstd[k];
@@ -167,32 +168,33 @@ int bnbwd_blocks(int M, int K)
 hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *mask,
                               const uint16_t *z, const float *gamma, const float *saved_mean,
                               const float *saved_invstd, float *part, double *pp, float *coef,
-                              float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st)
+                              float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const int B = bnbwd_blocks((int)M, K);
     const int rpp = NT / (K / 8);
     int rows = (int)((M + B - 1) / B);
     rows = (rows + rpp - 1) / rpp * rpp;
     const int Bn = (int)((M + rows - 1) / rows);
-    bnbwd_reduce_kernel<<<Bn, NT, 0, st>>>((const u32x4 *)dy, mask, (const u32x4 *)z, saved_mean, saved_invstd,
-                                           (int)M, K, rows, part);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(bnbwd_reduce_kernel, dim3(Bn), dim3(NT), 0, st, e0, nullptr, (const u32x4 *)dy, mask,
+                          (const u32x4 *)z, saved_mean, saved_invstd, (int)M, K, rows, part);
     if (e != hipSuccess) return e;
-    if ((e = launch_colsum(part, Bn, K, pp, st)) != hipSuccess) return e;
-    const int Gn = colsum_groups(Bn);
-    bnbwd_finalize_kernel<<<(K + NT - 1) / NT, NT, 0, st>>>(pp, Gn, K, (double)M, gamma, saved_invstd, coef, dgamma,
-                                                            dbeta);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (Bn <= COLSUM_DIRECT_ROWS) {
+        e = launch(bnbwd_finalize_kernel<float>, dim3(1), dim3(NT), 0, st, nullptr, nullptr, (const float *)part, Bn,
+                   K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
+    } else {
+        if ((e = launch_colsum(part, Bn, 2 * K, pp, st)) != hipSuccess) return e;
+        e = launch(bnbwd_finalize_kernel<double>, dim3(1), dim3(NT), 0, st, nullptr, nullptr, (const double *)pp,
+                   colsum_groups(Bn), K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
+    }
+    if (e != hipSuccess) return e;
     const int chunks = (int)(M * K / 8);
     const int cpr = K / 8;
     const int blocks = (chunks + NT * APPLY_UNROLL - 1) / (NT * APPLY_UNROLL);
     if (NT % cpr == 0)
-        bnbwd_apply_kernel<true><<<blocks, NT, 0, st>>>((const u32x4 *)dy, mask, (const u32x4 *)z, saved_mean,
-                                                        saved_invstd, coef, K, (u32x4 *)dz, chunks, cpr);
-    else
-        bnbwd_apply_kernel<false><<<blocks, NT, 0, st>>>((const u32x4 *)dy, mask, (const u32x4 *)z, saved_mean,
-                                                         saved_invstd, coef, K, (u32x4 *)dz, chunks, cpr);
-    return hipGetLastError();
+        return launch(bnbwd_apply_kernel<true>, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const u32x4 *)dy, mask,
+                      (const u32x4 *)z, saved_mean, saved_invstd, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
+    return launch(bnbwd_apply_kernel<false>, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const u32x4 *)dy, mask,
+                  (const u32x4 *)z, saved_mean, saved_invstd, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
 }
 
 }  // namespace cbr

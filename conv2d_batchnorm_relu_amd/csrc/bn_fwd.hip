@@ -1,62 +1,36 @@
 // bn_fwd.hip -- batch-norm finalize, normalise + ReLU + packed mask, and the BN fold.
 #include "cbr_launch.h"
+#include "cbr_reduce.h"
 
 namespace cbr {
 namespace {
 
 constexpr int NT = 256;
+constexpr int MAXK2 = 2 * 2048;
 
-// Column sums of a [B][2][K] fp32 partial array over B, in fp64 and a fixed order:
-// block b covers rows [b*bpb, (b+1)*bpb); when K <= 256 the threads split into 256/K
-// subgroups striding over the rows, combined in subgroup order.
-__global__ __launch_bounds__(NT) void colsum_stage1_kernel(const float *__restrict__ part, int B, int K, int bpb,
+// Stage 1 for many partial rows: block b folds rows [b*rpb, (b+1)*rpb) into pp[b][2K] (fp64).
+__global__ __launch_bounds__(NT) void colsum_stage1_kernel(const float *__restrict__ part, int R, int K2, int rpb,
                                                            double *__restrict__ pp)
 {
-    __shared__ double red[2][NT];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int t0 = b * bpb, t1 = min(B, t0 + bpb);
-    if (K <= NT) {
-        const int nsub = NT / K;
-        const int k = tid % K, sub = tid / K;
-        double s1 = 0.0, s2 = 0.0;
-        if (sub < nsub)
-            for (int t = t0 + sub; t < t1; t += nsub) {
-                s1 += part[(size_t)t * 2 * K + k];
-                s2 += part[(size_t)t * 2 * K + K + k];
-            }
-        red[0][tid] = s1;
-        red[1][tid] = s2;
-        __syncthreads();
-        if (tid < K) {
-            double a = 0.0, c = 0.0;
-            for (int s = 0; s < nsub; ++s) {
-                a += red[0][s * K + tid];
-                c += red[1][s * K + tid];
-            }
-            pp[(size_t)b * 2 * K + tid] = a;
-            pp[(size_t)b * 2 * K + K + tid] = c;
-        }
-    } else {
-        for (int k = tid; k < K; k += NT) {
-            double s1 = 0.0, s2 = 0.0;
-            for (int t = t0; t < t1; ++t) {
-                s1 += part[(size_t)t * 2 * K + k];
-                s2 += part[(size_t)t * 2 * K + K + k];
-            }
-            pp[(size_t)b * 2 * K + k] = s1;
-            pp[(size_t)b * 2 * K + K + k] = s2;
-        }
-    }
+    __shared__ double tot[MAXK2];
+    __shared__ double scratch[NT * 4];
+    const int r0 = blockIdx.x * rpb;
+    const int rows = min(rpb, R - r0);
+    sum_rows_to_lds<float>(part + (size_t)r0 * K2, rows, K2, tot, scratch);
+    for (int k2 = threadIdx.x; k2 < K2; k2 += NT) pp[(size_t)blockIdx.x * K2 + k2] = tot[k2];
 }
 
-// Stage 2: the BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per
-// channel: mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the
-// difference accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
+// The BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per channel:
+// mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the difference
+// accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
 // eq_bias = beta - gamma*mean*inv_std, and the running update
 // next = (1 - momentum)*prev + momentum*batch (BatchNorm CUDA page, section 2.4).
-// rm_out/rv_out may alias rm_in/rv_in: each thread reads its channel before writing it.
-__global__ __launch_bounds__(NT) void stats_finalize_kernel(const double *__restrict__ pp, int G, int K,
-                                                            double M, const float *__restrict__ gamma,
+// One block; the R partial rows ([R][2][K], sums then sums of squares) are summed
+// first.  rm_out/rv_out may alias rm_in/rv_in: each thread reads its channel before
+// writing it.
+template <typename TIn>
+__global__ __launch_bounds__(NT) void stats_finalize_kernel(const TIn *__restrict__ rows, int R, int K, double M,
+                                                            const float *__restrict__ gamma,
                                                             const float *__restrict__ beta, const float *rm_in,
                                                             const float *rv_in, float eps, float momentum,
                                                             float *__restrict__ scale, float *__restrict__ shift,
@@ -64,14 +38,12 @@ __global__ __launch_bounds__(NT) void stats_finalize_kernel(const double *__rest
                                                             float *__restrict__ saved_invstd, float *rm_out,
                                                             float *rv_out)
 {
-    for (int k = blockIdx.x * NT + threadIdx.x; k < K; k += gridDim.x * NT) {
-        double s1 = 0.0, s2 = 0.0;
-        for (int b = 0; b < G; ++b) {
-            s1 += pp[(size_t)b * 2 * K + k];
-            s2 += pp[(size_t)b * 2 * K + K + k];
-        }
-        const double mean = s1 / M;
-        double var = s2 / M - mean * mean;
+    __shared__ double tot[MAXK2];
+    __shared__ double scratch[NT * 4];
+    sum_rows_to_lds<TIn>(rows, R, 2 * K, tot, scratch);
+    for (int k = threadIdx.x; k < K; k += NT) {
+        const double mean = tot[k] / M;
+        double var = tot[K + k] / M - mean * mean;
         if (!(var > 0.0)) var = 0.0;
         const double invstd = 1.0 / sqrt(var + (double)eps);
         const double gm = (double)gamma[k];
@@ -170,64 +142,71 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
     }
 }
 
+int colsum_rows_per_group(int R)
+{
+    const int G = std::min(COLSUM_MAX_GROUPS, R);
+    return (R + G - 1) / G;
+}
+
 }  // namespace
 
-static int colsum_rows_per_group(int B)
+int colsum_groups(int R)
 {
-    const int G = std::min(COLSUM_MAX_GROUPS, B);
-    return (B + G - 1) / G;
+    const int rpb = colsum_rows_per_group(R);
+    return (R + rpb - 1) / rpb;
 }
 
-int colsum_groups(int B)
+hipError_t launch_colsum(const float *part, int R, int K2, double *pp, hipStream_t st, hipEvent_t e0)
 {
-    const int bpb = colsum_rows_per_group(B);
-    return (B + bpb - 1) / bpb;
+    return launch(colsum_stage1_kernel, dim3(colsum_groups(R)), dim3(NT), 0, st, e0, nullptr, part, R, K2,
+                  colsum_rows_per_group(R), pp);
 }
 
-hipError_t launch_colsum(const float *part, int B, int K, double *pp, hipStream_t st)
+int train_partial_rows(const ConvGeom &g)
 {
-    const int bpb = colsum_rows_per_group(B);
-    colsum_stage1_kernel<<<colsum_groups(B), NT, 0, st>>>(part, B, K, bpb, pp);
-    return hipGetLastError();
+    return halo_eligible(g) ? halo_grid(g) : conv_plan(g).tiles_m;
 }
 
-hipError_t launch_stats_finalize(int tiles_m, int K, long M, const float *partials, double *pp,
+hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, double *pp,
                                  const float *gamma, const float *beta, const float *rm_in,
                                  const float *rv_in, float eps, float momentum, float *scale,
                                  float *shift, float *saved_mean, float *saved_invstd,
-                                 float *rm_out, float *rv_out, hipStream_t st)
+                                 float *rm_out, float *rv_out, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    hipError_t e = launch_colsum(partials, tiles_m, K, pp, st);
+    if (rows <= COLSUM_DIRECT_ROWS)
+        return launch(stats_finalize_kernel<float>, dim3(1), dim3(NT), 0, st, e0, e1, partials, rows, K, (double)M,
+                      gamma, beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out,
+                      rv_out);
+    const int G = colsum_groups(rows);
+    hipError_t e = launch_colsum(partials, rows, 2 * K, pp, st, e0);
     if (e != hipSuccess) return e;
-    stats_finalize_kernel<<<(K + NT - 1) / NT, NT, 0, st>>>(pp, colsum_groups(tiles_m), K, (double)M, gamma, beta,
-                                                            rm_in, rv_in, eps, momentum, scale, shift, saved_mean,
-                                                            saved_invstd, rm_out, rv_out);
-    return hipGetLastError();
+    return launch(stats_finalize_kernel<double>, dim3(1), dim3(NT), 0, st, nullptr, e1, (const double *)pp, G, K,
+                  (double)M, gamma, beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out,
+                  rv_out);
 }
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,
-                                     const float *shift, uint16_t *y, uint8_t *mask, hipStream_t st)
+                                     const float *shift, uint16_t *y, uint8_t *mask, hipStream_t st,
+                                     hipEvent_t e0, hipEvent_t e1)
 {
     const int chunks = (int)(M * K / 8);
     const int cpr = K / 8;
     const int blocks = (chunks + NT * APPLY_UNROLL - 1) / (NT * APPLY_UNROLL);
     if (NT % cpr == 0)
-        bn_apply_relu_mask_kernel<true><<<blocks, NT, 0, st>>>((const u32x4 *)z, scale, shift, (u32x4 *)y,
-                                                               mask, chunks, cpr);
-    else
-        bn_apply_relu_mask_kernel<false><<<blocks, NT, 0, st>>>((const u32x4 *)z, scale, shift, (u32x4 *)y,
-                                                                mask, chunks, cpr);
-    return hipGetLastError();
+        return launch(bn_apply_relu_mask_kernel<true>, dim3(blocks), dim3(NT), 0, st, e0, e1, (const u32x4 *)z,
+                      scale, shift, (u32x4 *)y, mask, chunks, cpr);
+    return launch(bn_apply_relu_mask_kernel<false>, dim3(blocks), dim3(NT), 0, st, e0, e1, (const u32x4 *)z, scale,
+                  shift, (u32x4 *)y, mask, chunks, cpr);
 }
 
 hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, const float *gamma,
                           const float *beta, const float *rm, const float *rv, float eps,
-                          uint16_t *w_fold, float *b_fold, hipStream_t st)
+                          uint16_t *w_fold, float *b_fold, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const long total = (long)K * Kg;
     const int blocks = (int)std::min<long>((total + NT - 1) / NT, 4096);
-    bn_fold_kernel<<<blocks, NT, 0, st>>>(w, bias, gamma, beta, rm, rv, eps, K, Kg, w_fold, b_fold);
-    return hipGetLastError();
+    return launch(bn_fold_kernel, dim3(blocks), dim3(NT), 0, st, e0, e1, w, bias, gamma, beta, rm, rv, eps, K, Kg,
+                  w_fold, b_fold);
 }
 
 }  // namespace cbr

@@ -61,10 +61,9 @@ struct BwdLayout { size_t dz, part, pp, coef, wpart, wflip, total; };
 
 TrainLayout train_layout(const ConvGeom &g)
 {
-    const ConvPlan p = conv_plan(g);
     TrainLayout L;
     size_t o = 0;
-    L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)p.tiles_m);
+    L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)train_partial_rows(g));
     L.pp = o; o = align_up(o + sizeof(double) * 2 * g.K * (size_t)COLSUM_MAX_GROUPS);
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
@@ -107,11 +106,8 @@ bool any_null(T... ps) { return ((ps == nullptr) || ...); }
 
 char *ws_at(void *ws, size_t off) { return (char *)ws + off; }
 
-// Records events[i] on the stream when profiling events were supplied.
-bool mark(void *const *events, int i, hipStream_t s)
-{
-    return !events || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
-}
+// Profiling event i, or none.
+hipEvent_t ev(void *const *events, int i) { return events ? (hipEvent_t)events[i] : nullptr; }
 
 }  // namespace
 
@@ -187,19 +183,19 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
     double *pp = (double *)ws_at(workspace, L.pp);
     float *scale = (float *)ws_at(workspace, L.scale);
     float *shift = (float *)ws_at(workspace, L.shift);
-    const ConvPlan p = conv_plan(g);
-    // conv + per-tile channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
-    if (!mark(events, 0, s)) return CBR_E_HIP;
-    if (launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s) != hipSuccess) return CBR_E_HIP;
-    if (!mark(events, 1, s)) return CBR_E_HIP;
-    if (launch_stats_finalize(p.tiles_m, g.K, g.M, partials, pp, gamma, beta, run_mean_in, run_var_in, eps,
-                              momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out,
-                              s) != hipSuccess)
+    // conv + channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
+    const hipError_t ec = halo_eligible(g)
+                              ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
+                              : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
+                                                  ev(events, 1));
+    if (ec != hipSuccess) return CBR_E_HIP;
+    if (launch_stats_finalize(train_partial_rows(g), g.K, g.M, partials, pp, gamma, beta, run_mean_in, run_var_in,
+                              eps, momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out, s,
+                              ev(events, 2), ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
-    if (!mark(events, 2, s)) return CBR_E_HIP;
-    if (launch_bn_apply_relu_mask(g.M, g.K, z, scale, shift, y, (uint8_t *)relu_mask, s) != hipSuccess)
+    if (launch_bn_apply_relu_mask(g.M, g.K, z, scale, shift, y, (uint8_t *)relu_mask, s, ev(events, 4),
+                                  ev(events, 5)) != hipSuccess)
         return CBR_E_HIP;
-    if (!mark(events, 3, s)) return CBR_E_HIP;
     return CBR_OK;
 }
 
@@ -233,12 +229,11 @@ int cbr_forward_infer_ev(const cbr_shape *shape, const uint16_t *x, const uint16
     hipStream_t s = (hipStream_t)stream;
     uint16_t *wf = (uint16_t *)ws_at(workspace, L.wfold);
     float *bf = (float *)ws_at(workspace, L.bfold);
-    if (!mark(events, 0, s)) return CBR_E_HIP;
-    if (launch_bn_fold(g.K, g.Kg, w, conv_bias, gamma, beta, run_mean, run_var, eps, wf, bf, s) != hipSuccess)
+    if (launch_bn_fold(g.K, g.Kg, w, conv_bias, gamma, beta, run_mean, run_var, eps, wf, bf, s, ev(events, 0),
+                       ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    if (!mark(events, 1, s)) return CBR_E_HIP;
-    if (launch_conv_fprop(g, EPI_BIAS_RELU, x, wf, bf, y, nullptr, s) != hipSuccess) return CBR_E_HIP;
-    if (!mark(events, 2, s)) return CBR_E_HIP;
+    if (launch_conv_fprop(g, EPI_BIAS_RELU, x, wf, bf, y, nullptr, s, ev(events, 2), ev(events, 3)) != hipSuccess)
+        return CBR_E_HIP;
     return CBR_OK;
 }
 
@@ -273,21 +268,24 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
     // masked BN backward (CBR page 5.1) -> WGrad -> DGrad (5.2; skipped for the first layer, 5.3).
     // WGrad is enqueued before DGrad on the same stream, so it has finished reading x
     // before DGrad may overwrite it when dx aliases x.
-    if (!mark(events, 0, s)) return CBR_E_HIP;
     if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
                            (float *)ws_at(workspace, L.part), (double *)ws_at(workspace, L.pp),
-                           (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s) != hipSuccess)
+                           (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s, ev(events, 0),
+                           ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    if (!mark(events, 1, s)) return CBR_E_HIP;
-    if (launch_conv_wgrad(g, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s) != hipSuccess) return CBR_E_HIP;
-    if (!mark(events, 2, s)) return CBR_E_HIP;
+    if (launch_conv_wgrad(g, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s, ev(events, 2), ev(events, 3)) !=
+        hipSuccess)
+        return CBR_E_HIP;
     if (dx) {
         uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
-        if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s) != hipSuccess) return CBR_E_HIP;
+        if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, ev(events, 4), nullptr) != hipSuccess) return CBR_E_HIP;
         const ConvGeom d = dgrad_geom(g);
-        if (launch_conv_fprop(d, EPI_PLAIN, dzp, wt, nullptr, dx, nullptr, s) != hipSuccess) return CBR_E_HIP;
+        if (launch_conv_fprop(d, EPI_PLAIN, dzp, wt, nullptr, dx, nullptr, s, nullptr, ev(events, 5)) != hipSuccess)
+            return CBR_E_HIP;
+    } else if (events && (hipEventRecord(ev(events, 4), s) != hipSuccess ||
+                          hipEventRecord(ev(events, 5), s) != hipSuccess)) {
+        return CBR_E_HIP;
     }
-    if (!mark(events, 3, s)) return CBR_E_HIP;
     return CBR_OK;
 }
 

@@ -20,14 +20,18 @@ struct ConvGeom {
     int Kg;           // R*S*C (GEMM reduction length)
 };
 
-// Round-to-nearest-even float -> bfloat16 bit pattern (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bfloat16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// Round-to-nearest-even float -> bfloat16 bit pattern.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
 {
@@ -37,8 +41,3 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
 // Low / high bf16 of a packed 32-bit word, widened to float.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}

@@ -1,15 +1,35 @@
 // cbr_launch.h -- host-side plan and launch functions of the CBR kernels (internal).
+//
+// Every launch function takes an optional pair of events (e0, e1): when either is set,
+// the first kernel of the stage is launched with hipExtLaunchKernelGGL recording e0 at
+// its start and the last kernel records e1 at its end, so the events bracket exactly
+// the stage's kernels (no extra marker packets in the stream).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "cbr_common.h"
 
 namespace cbr {
 
 enum ConvEpilogue { EPI_STATS = 0, EPI_BIAS_RELU = 1, EPI_PLAIN = 2 };
+
+// Launches kernel k, recording e0 at its start and e1 at its end when either is set.
+template <typename Kern, typename... Args>
+inline hipError_t launch(Kern k, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, hipEvent_t e0,
+                         hipEvent_t e1, Args... args)
+{
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(k, grid, block, shmem, st, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(k, grid, block, shmem, st, args...);
+    return hipGetLastError();
+}
 
 // Tile plan of the implicit-GEMM convolution: BM output pixels x BN output channels
 // per workgroup.  The plan is a pure function of the geometry, so workspace sizing and
@@ -21,12 +41,24 @@ struct ConvPlan {
 };
 ConvPlan conv_plan(const ConvGeom &g);
 
-// Column sums of a [B][2][K] fp32 partial array: stage 1 folds the B rows into
-// colsum_groups(B) <= 64 fp64 rows pp[G][2][K] (fixed order); finalize kernels then
-// sum those G rows per channel.
+// Persistent 3x3 / stride 1 / pad 1, 64 -> 64 channel convolution + channel statistics.
+constexpr int HALO_MAX_GRID = 256;                        // one workgroup per MI355X CU
+constexpr int HALO_MAX_LDS = 64 * 1168 + 10 * (56 + 2) * 144;  // filter + input-row ring, W <= 56
+bool halo_eligible(const ConvGeom &g);
+int halo_grid(const ConvGeom &g);
+size_t halo_lds_bytes(const ConvGeom &g);
+hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
+                                    float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+
+// Rows of per-channel partial sums the training forward produces (one [2][K] row each).
+int train_partial_rows(const ConvGeom &g);
+
+// Column sums of a [R][2K] fp32 partial array are folded in two stages when R is large:
+// colsum_groups(R) <= 64 rows of fp64 partial sums, then the finalize kernel.
 constexpr int COLSUM_MAX_GROUPS = 64;
-int colsum_groups(int B);
-hipError_t launch_colsum(const float *part, int B, int K, double *pp, hipStream_t st);
+constexpr int COLSUM_DIRECT_ROWS = 512;   // up to this many rows the finalize reads them directly
+int colsum_groups(int R);
+hipError_t launch_colsum(const float *part, int R, int K2, double *pp, hipStream_t st, hipEvent_t e0 = nullptr);
 
 // Blocks of the BN-backward reduction over M rows of K channels.
 int bnbwd_blocks(int M, int K);
@@ -40,30 +72,36 @@ struct WgradPlan {
 WgradPlan wgrad_plan(int M, int K, int Kg);
 
 hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w,
-                             const float *bias, uint16_t *out, float *partials, hipStream_t st);
+                             const float *bias, uint16_t *out, float *partials, hipStream_t st,
+                             hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-hipError_t launch_stats_finalize(int tiles_m, int K, long M, const float *partials, double *pp,
+hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, double *pp,
                                  const float *gamma, const float *beta, const float *rm_in,
                                  const float *rv_in, float eps, float momentum, float *scale,
                                  float *shift, float *saved_mean, float *saved_invstd,
-                                 float *rm_out, float *rv_out, hipStream_t st);
+                                 float *rm_out, float *rv_out, hipStream_t st,
+                                 hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,
-                                     const float *shift, uint16_t *y, uint8_t *mask, hipStream_t st);
+                                     const float *shift, uint16_t *y, uint8_t *mask, hipStream_t st,
+                                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, const float *gamma,
                           const float *beta, const float *rm, const float *rv, float eps,
-                          uint16_t *w_fold, float *b_fold, hipStream_t st);
+                          uint16_t *w_fold, float *b_fold, hipStream_t st,
+                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *mask,
                               const uint16_t *z, const float *gamma, const float *saved_mean,
                               const float *saved_invstd, float *part, double *pp, float *coef,
-                              float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st);
+                              float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st,
+                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt,
-                               hipStream_t st);
+                               hipStream_t st, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16_t *x,
-                             float *part, float *dw, hipStream_t st);
+                             float *part, float *dw, hipStream_t st,
+                             hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 }  // namespace cbr

@@ -247,14 +247,14 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
 }
 
 template <int BM, int BN, bool VEC>
-hipError_t launch_epi(const ConvGeom &g, int epi, const ConvParams &prm, dim3 grid, hipStream_t st)
+hipError_t launch_epi(int epi, const ConvParams &prm, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     switch (epi) {
-    case EPI_STATS: conv_fprop_kernel<BM, BN, VEC, EPI_STATS><<<grid, NT, 0, st>>>(prm); break;
-    case EPI_BIAS_RELU: conv_fprop_kernel<BM, BN, VEC, EPI_BIAS_RELU><<<grid, NT, 0, st>>>(prm); break;
-    default: conv_fprop_kernel<BM, BN, VEC, EPI_PLAIN><<<grid, NT, 0, st>>>(prm); break;
+    case EPI_STATS: return launch(conv_fprop_kernel<BM, BN, VEC, EPI_STATS>, grid, dim3(NT), 0, st, e0, e1, prm);
+    case EPI_BIAS_RELU:
+        return launch(conv_fprop_kernel<BM, BN, VEC, EPI_BIAS_RELU>, grid, dim3(NT), 0, st, e0, e1, prm);
+    default: return launch(conv_fprop_kernel<BM, BN, VEC, EPI_PLAIN>, grid, dim3(NT), 0, st, e0, e1, prm);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -271,17 +271,18 @@ ConvPlan conv_plan(const ConvGeom &g)
 }
 
 hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w,
-                             const float *bias, uint16_t *out, float *partials, hipStream_t st)
+                             const float *bias, uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0,
+                             hipEvent_t e1)
 {
     const ConvPlan p = conv_plan(g);
     ConvParams prm{g, x, w, bias, out, partials};
     dim3 grid(p.tiles_m, p.tiles_n);
     if (p.bn == 128) {
-        return p.vec ? launch_epi<128, 128, true>(g, epi, prm, grid, st)
-                     : launch_epi<128, 128, false>(g, epi, prm, grid, st);
+        return p.vec ? launch_epi<128, 128, true>(epi, prm, grid, st, e0, e1)
+                     : launch_epi<128, 128, false>(epi, prm, grid, st, e0, e1);
     }
-    return p.vec ? launch_epi<128, 64, true>(g, epi, prm, grid, st)
-                 : launch_epi<128, 64, false>(g, epi, prm, grid, st);
+    return p.vec ? launch_epi<128, 64, true>(epi, prm, grid, st, e0, e1)
+                 : launch_epi<128, 64, false>(epi, prm, grid, st, e0, e1);
 }
 
 }  // namespace cbr

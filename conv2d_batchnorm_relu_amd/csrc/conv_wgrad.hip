@@ -248,33 +248,32 @@ WgradPlan wgrad_plan(int M, int K, int Kg)
 }
 
 hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16_t *x, float *part, float *dw,
-                             hipStream_t st)
+                             hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const WgradPlan p = wgrad_plan(g.M, g.K, g.Kg);
     WgradParams prm{g, dz, x, p.splits == 1 ? dw : part, p.rows_per_split};
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
     const bool vec = (g.C % 8) == 0;
-    if (p.bm == 128) {
-        if (vec) conv_wgrad_kernel<128, 128, true><<<grid, NT, 0, st>>>(prm);
-        else conv_wgrad_kernel<128, 128, false><<<grid, NT, 0, st>>>(prm);
-    } else {
-        if (vec) conv_wgrad_kernel<64, 128, true><<<grid, NT, 0, st>>>(prm);
-        else conv_wgrad_kernel<64, 128, false><<<grid, NT, 0, st>>>(prm);
-    }
-    hipError_t e = hipGetLastError();
+    const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;   // end event on the last kernel of the stage
+    hipError_t e;
+    if (p.bm == 128)
+        e = vec ? launch(conv_wgrad_kernel<128, 128, true>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<128, 128, false>, grid, dim3(NT), 0, st, e0, ek, prm);
+    else
+        e = vec ? launch(conv_wgrad_kernel<64, 128, true>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<64, 128, false>, grid, dim3(NT), 0, st, e0, ek, prm);
     if (e != hipSuccess || p.splits == 1) return e;
     const long n = (long)g.K * g.Kg;
     const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);
-    split_sum_kernel<<<blocks, NT, 0, st>>>(part, p.splits, n, dw);
-    return hipGetLastError();
+    return launch(split_sum_kernel, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const float *)part, p.splits, n, dw);
 }
 
-hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt, hipStream_t st)
+hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt, hipStream_t st,
+                               hipEvent_t e0, hipEvent_t e1)
 {
     const long total = (long)K * R * S * C;
     const int blocks = (int)std::min<long>((total + NT - 1) / NT, 4096);
-    flip_weights_kernel<<<blocks, NT, 0, st>>>(w, K, R, S, C, wt);
-    return hipGetLastError();
+    return launch(flip_weights_kernel, dim3(blocks), dim3(NT), 0, st, e0, e1, w, K, R, S, C, wt);
 }
 
 }  // namespace cbr

@@ -154,14 +154,15 @@ int cbr_backward(const cbr_shape *shape,
 
 /*
  * Timed variants for profiling: identical to the calls above, and in addition record
- * caller-created hipEvent_t handles (passed as void*) on `stream` around each kernel
- * stage, so a caller can time the stages with hipEventElapsedTime.  `events` may be
- * NULL (then the call is exactly the untimed one).  Events recorded:
- *   train:  [0] before the convolution, [1] after it, [2] after the statistics
- *           finalize, [3] after normalise + ReLU + mask                 (4 events)
- *   infer:  [0] before the fold, [1] after it, [2] after the convolution (3 events)
- *   bwd:    [0] before the BN backward, [1] after it (dz ready), [2] after the weight
- *           gradient, [3] after the data gradient (== [2] when dx is NULL) (4 events)
+ * caller-created hipEvent_t handles (passed as void*) at the start of the first kernel
+ * and the end of the last kernel of each stage (taken from the kernels' own dispatch
+ * timestamps, so no marker packets are added to the stream).  `events` may be NULL
+ * (then the call is exactly the untimed one).  Event pairs (start, end):
+ *   train:  [0,1] convolution + channel sums, [2,3] statistics finalize,
+ *           [4,5] normalise + ReLU + mask                                  (6 events)
+ *   infer:  [0,1] fold, [2,3] convolution + bias + ReLU                     (4 events)
+ *   bwd:    [0,1] BN backward (reduce, finalize, dz), [2,3] weight gradient,
+ *           [4,5] data gradient (recorded back to back when dx is NULL)    (6 events)
  */
 int cbr_forward_train_ev(const cbr_shape *shape,
                          const uint16_t *x, const uint16_t *w,

@@ -42,6 +42,27 @@ def test_train_forward_small(g):
     H.check_train(g, d, res, ora)
 
 
+# The persistent 3x3 / 64-channel kernel: partial last steps, several images per
+# workgroup (N > 256), short and narrow images.
+HALO_GEOMS = [
+    Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1),     # 8 + 4 output rows
+    Geometry(3, 9, 20, 64, 64, 3, 3, 1, 1),      # 160-pixel steps (5 blocks)
+    Geometry(1, 56, 56, 64, 64, 3, 3, 1, 1),     # one full image, seven steps
+    Geometry(300, 5, 7, 64, 64, 3, 3, 1, 1),     # two images for some workgroups, partial blocks
+    Geometry(2, 3, 56, 64, 64, 3, 3, 1, 1),      # fewer rows than a step
+    Geometry(2, 17, 2, 64, 64, 3, 3, 1, 1),      # the narrowest image
+]
+
+
+@pytest.mark.parametrize("g", HALO_GEOMS, ids=str)
+def test_train_forward_persistent_3x3(g):
+    H.log(f"train fwd (persistent 3x3) {g}")
+    d = draw(g, "train", 14)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
 @pytest.mark.parametrize("g", INFER_GEOMS, ids=str)
 def test_infer_small(g):
     H.log(f"infer {g}")
@@ -161,3 +182,26 @@ def test_backward_full_workload():
     H.log("oracle")
     ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"])
     H.check_backward(g, d, bw, ob)
+
+
+@pytest.mark.parametrize("g", [Geometry(2, 6, 10, 8, 8, 1, 1, 1, 0),        # generic kernel
+                               Geometry(2, 6, 10, 64, 64, 3, 3, 1, 1)],     # persistent 3x3 kernel
+                         ids=["generic", "persistent3x3"])
+def test_z_rounding_is_nearest_even(g):
+    """z = x0 + x1 with x0 = 1 + j*2^-7 and x1 in {2^-8, 3*2^-8, 2^-9}: exact fp32 sums that sit
+    on (or next to) bf16 rounding ties; the stored z must be their round-to-nearest-even."""
+    from conv2d_batchnorm_relu_amd.inputs import bf16_round
+    rng = np.random.default_rng(15)
+    x = np.zeros((g.n, g.h, g.w, g.c), np.float32)
+    x[..., 0] = 1.0 + rng.integers(0, 8, (g.n, g.h, g.w)) * 2.0 ** -7
+    x[..., 1] = rng.choice(np.array([2.0 ** -8, 3 * 2.0 ** -8, 2.0 ** -9], np.float32), (g.n, g.h, g.w))
+    w = np.zeros((g.k, g.r, g.s, g.c), np.float32)
+    w[:, g.r // 2, g.s // 2, 0] = 1.0
+    w[:, g.r // 2, g.s // 2, 1] = 1.0
+    d = draw(g, "train", 16)
+    d["x"], d["w"] = x, w
+    res, _ = H.gpu_train(g, d)
+    exact = (x[..., 0] + x[..., 1]).astype(np.float32)              # exact in fp32
+    want = np.broadcast_to(bf16_round(exact)[..., None], res["z"].shape)
+    np.testing.assert_array_equal(res["z"], want)
+    assert (bf16_round(exact) != exact).any()                         # ties were really exercised
