@@ -15,6 +15,7 @@ the host as a reported baseline (unless --no-cpu-baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -82,16 +83,50 @@ def kernel_entry(name, ms, nbytes, flops):
             "bytes": int(nbytes), "flops": int(flops)}
 
 
-def roofline_of(entry):
+# Sources of the persistent 3x3 kernel: measured HBM traffic stored under profiles/ is
+# reported only while these files are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv3x3_c64_stats_n256_56x56.json")
+KERNEL_SOURCES = ["conv2d_batchnorm_relu_amd/csrc/conv3x3_c64.hip", "conv2d_batchnorm_relu_amd/csrc/cbr_common.h",
+                  "conv2d_batchnorm_relu_amd/csrc/cbr_launch.h"]
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the persistent conv from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factors), or None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_digest():
+        return None
+    return int(t["traffic_bytes_per_launch"])
+
+
+def roofline_of(entry, traffic=None):
     """The kernel's binding roofline: whichever of HBM bytes and MFMA flops needs more
     time at peak."""
     t_hbm = entry["bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = entry["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     if t_mfma > t_hbm:
         return {"kernel": entry["kernel"], "bound": "mfma", "achieved": entry["tflops"],
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": entry["mfma_frac"], "traffic": None}
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": entry["mfma_frac"], "traffic": traffic}
     return {"kernel": entry["kernel"], "bound": "hbm", "achieved": entry["gbps"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": entry["hbm_frac"], "traffic": None}
+            "unit": "GB/s", "frac": entry["hbm_frac"], "traffic": traffic}
+
+
+def pct(vals, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(vals), q))
 
 
 def main():
@@ -104,6 +139,10 @@ def main():
     ap.add_argument("--cpu-images", type=int, default=256,
                     help="images of the headline workload the CPU oracle runs (of 256)")
     ap.add_argument("--cold", type=int, default=5, help="steps timed after evicting the caches")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-box copy and matmul peak runs")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device three times (the known-size "
+                         "copy that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported here (this operator's "
@@ -138,7 +177,7 @@ def main():
     def timed(fn, nev, steps, warmup):
         """Runs fn warmup times, then `steps` timed calls without events (wall clock,
         bracketed by device synchronisation), then `steps` calls with per-stage kernel
-        events; returns (ms per call, [mean ms per stage])."""
+        events; returns (ms per call, [mean ms per stage], [[ms per call] per stage])."""
         for _ in range(warmup):
             fn(None)
         torch.cuda.synchronize()
@@ -152,9 +191,12 @@ def main():
         for i in range(steps):
             fn(evs[i])
         torch.cuda.synchronize()
-        stages = [sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(steps)) / steps
-                  for j in range(nev // 2)]
-        return wall, stages
+        per = [[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(steps)] for j in range(nev // 2)]
+        stages = [sum(v) / steps for v in per]
+        return wall, stages, per
+
+    def spread(vals):
+        return {"median": round(pct(vals, 50), 5), "p10": round(pct(vals, 10), 5), "p90": round(pct(vals, 90), 5)}
 
     # ---------------- headline: training forward ----------------
     log("drawing the headline workload")
@@ -176,10 +218,10 @@ def main():
                               rmo, rvo, ws, events=events)
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms, stages = timed(train_step, 6, args.steps, args.warmup)
+    ms, stages, per = timed(train_step, 6, args.steps, args.warmup)
     flops = conv_flops(g)
     kb = train_bytes(g)
-    kernels = [kernel_entry("conv_fprop_stats", stages[0], kb["conv_fprop_stats"], flops),
+    kernels = [kernel_entry("conv3x3_c64_stats", stages[0], kb["conv_fprop_stats"], flops),
                kernel_entry("bn_stats_finalize", stages[1], 0, 0),
                kernel_entry("bn_apply_relu_mask", stages[2], kb["bn_apply_relu_mask"], 0)]
     dominant = max(kernels, key=lambda e: e["ms"])
@@ -219,8 +261,9 @@ def main():
         "step_roofline_frac": round(total_bytes / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4),
         "bytes_per_step": int(total_bytes),
         "unfused_bytes": int(unfused_train_bytes(g)),
-        "roofline": roofline_of(dominant),
+        "roofline": roofline_of(dominant, measured_traffic() if dominant is kernels[0] else None),
         "kernels": kernels,
+        "kernel_ms_spread": {e["kernel"]: spread(v) for e, v in zip(kernels, per)},
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
     }
     del z, y, mask, ws, x
@@ -243,7 +286,7 @@ def main():
             cbr.cbr_forward_infer(sp4, t4["x"], t4["w"], t4["b"], t4["ga"], t4["be"], t4["rm"], t4["rv"],
                                   wl4.eps, t4["y"], t4["ws"], events=events)
 
-        ms4, st4 = timed(infer_step, 4, steps, 5)
+        ms4, st4, _ = timed(infer_step, 4, steps, 5)
         ib = infer_bytes(g4)
         aux["infer"] = {"workload": "infer N256 28x28 C128->K128 3x3 s1 p1 (conv bias)", "ms": round(ms4, 5),
                         "tflops": round(conv_flops(g4) / (ms4 * 1e-3) / 1e12, 2),
@@ -279,7 +322,7 @@ def main():
             cbr.cbr_backward(sp5, t5["x"], t5["w"], zz, mk, t5["dy"], t5["ga"], s5m, s5i, dz, dgam, dbet, dw,
                              dx, ws5, events=events)
 
-        ms5, st5 = timed(bwd_step, 6, steps, 5)
+        ms5, st5, _ = timed(bwd_step, 6, steps, 5)
         bb = bwd_bytes(g5)
         f5 = conv_flops(g5)
         aux["backward"] = {"workload": "backward N256 14x14 C256->K256 3x3 s1 p1", "ms": round(ms5, 5),
@@ -287,7 +330,7 @@ def main():
                            "kernels": [kernel_entry("bn_backward", st5[0], bb["bn_backward"], 0),
                                        kernel_entry("conv_wgrad", st5[1], bb["conv_wgrad"], f5),
                                        kernel_entry("conv_dgrad", st5[2], bb["conv_dgrad"], f5)]}
-        ms5f, st5f = timed(fwd5, 6, steps, 5)
+        ms5f, st5f, _ = timed(fwd5, 6, steps, 5)
         aux["train_s4"] = {"workload": "train forward N256 14x14 C256->K256 3x3", "ms": round(ms5f, 5),
                            "tflops": round(f5 / (ms5f * 1e-3) / 1e12, 2)}
         del t5, zz, yy, mk, ws5, dz, dx
@@ -308,7 +351,7 @@ def main():
             cbr.cbr_forward_train(sp2, t2["x"], t2["w"], t2["ga"], t2["be"], t2["rm"], t2["rv"], wl2.eps,
                                   wl2.momentum, z2, y2, m2, v2[0], v2[1], v2[2], v2[3], ws2, events=events)
 
-        ms2, st2 = timed(stem_step, 6, steps, 5)
+        ms2, st2, _ = timed(stem_step, 6, steps, 5)
         kb2 = train_bytes(g2)
         aux["stem_train"] = {"workload": "train forward N64 224x224 C3->K64 7x7 s2 p3", "ms": round(ms2, 5),
                              "gbps": round(sum(kb2.values()) / (ms2 * 1e-3) / 1e9, 1),
@@ -318,6 +361,47 @@ def main():
                                          kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0)]}
         del t2, z2, y2, m2, ws2
         out["aux"] = aux
+
+    # ---------------- on-box peaks: streaming copy and a large bf16 matmul ----------------
+    if not args.no_peaks:
+        log("on-box peaks")
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        def ev_time(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ts = []
+            for _ in range(reps):
+                e0.record(); fn(); e1.record(); torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return pct(ts, 50)
+        t_copy = ev_time(lambda: dst.copy_(src), 10)
+        del src, dst
+        a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        t_mm = ev_time(lambda: torch.matmul(a, b), 10)
+        del a, b
+        copy_gbs = 2 * nb / (t_copy * 1e-3) / 1e9
+        mm_tfl = 2 * 8192 ** 3 / (t_mm * 1e-3) / 1e12
+        r = out["roofline"]
+        box_peak = copy_gbs if r["unit"] == "GB/s" else mm_tfl
+        out["onbox_peaks"] = {"copy_gbps": round(copy_gbs, 1), "bf16_matmul_tflops": round(mm_tfl, 1),
+                              "copy": "1 GiB device-to-device copy (read + write bytes)",
+                              "matmul": "torch.matmul bf16 8192^3 (hipBLASLt)",
+                              "dominant_frac_of_onbox_peak": round(r["achieved"] / box_peak, 4)}
+        torch.cuda.empty_cache()
+
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(5)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- CPU baseline: the fp64 oracle on the host ----------------
     if not args.no_cpu_baseline:
@@ -335,6 +419,20 @@ def main():
                                "cores": oracle.num_threads(), "kind": "oracle",
                                "sample": f"train forward on {n} of {g.n} images of the headline workload "
                                          f"(fp64 direct loops), {dt:.2f} s"}
+        # the same oracle on one thread, on a smaller sample
+        n1 = max(1, n // 16)
+        g1 = g.with_n(n1)
+        o1 = oracle.OShape(g1.n, g1.h, g1.w, g1.c, g1.k, g1.r, g1.s, g1.stride, g1.stride, g1.pad, g1.pad)
+        nthreads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t0 = time.perf_counter()
+        oracle.forward_train(o1, sub["x"][:n1], sub["w"], sub["gamma"], sub["beta"], sub["run_mean"],
+                             sub["run_var"], wl.eps, wl.momentum)
+        dt1 = time.perf_counter() - t0
+        oracle.set_num_threads(nthreads)
+        out["cpu_baseline_1thread"] = {"value": round(conv_flops(g1) / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                                       "cores": 1, "kind": "oracle",
+                                       "sample": f"train forward on {n1} of {g.n} images, {dt1:.2f} s"}
     print(json.dumps(out), flush=True)
 
 

@@ -65,6 +65,8 @@ def _load():
         lib.cbro_conv2d_wgrad.argtypes = _GEOM + [_D, _D, _D]
         lib.cbro_backward.argtypes = _GEOM + [_D, _D, _D, _U8, _D, _D, _D, _D, _D, _D, _D, _D, _D]
         lib.cbro_num_threads.restype = ctypes.c_int
+        lib.cbro_set_num_threads.argtypes = [ctypes.c_int]
+        lib.cbro_set_num_threads.restype = None
         for f in ("cbro_conv2d", "cbro_conv2d_at", "cbro_batch_stats", "cbro_forward_train",
                   "cbro_forward_infer", "cbro_fold", "cbro_bn_backward", "cbro_conv2d_dgrad",
                   "cbro_conv2d_wgrad", "cbro_backward"):
@@ -93,6 +95,11 @@ def _g(sp: OShape):
 
 def num_threads() -> int:
     return _load().cbro_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only: results do not depend on it)."""
+    _load().cbro_set_num_threads(int(n))
 
 
 def conv2d(sp: OShape, x, w, bias=None):

@@ -340,3 +340,14 @@ int cbro_num_threads(void)
 #endif
     return t;
 }
+
+/* Sets the number of OpenMP threads later calls use (n >= 1); timing only, the results
+ * do not depend on it (every output element is computed by one thread, in a fixed order). */
+void cbro_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
