@@ -81,18 +81,19 @@ __global__ __launch_bounds__(NT) void bnbwd_reduce_kernel(const u32x4 *__restric
 
 // dbeta = s1, dgamma = s2 (fp64 over the partial rows, fixed order); coefficients of
 // the apply step: coef[0] = gamma*invstd, coef[1] = dbeta/M, coef[2] = dgamma/M.
-template <typename TIn>
-__global__ __launch_bounds__(NT) void bnbwd_finalize_kernel(const TIn *__restrict__ rows, int R, int K, double M,
+// Block b owns channels 4b..4b+3.
+__global__ __launch_bounds__(NT) void bnbwd_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
                                                             const float *__restrict__ gamma,
                                                             const float *__restrict__ invstd,
                                                             float *__restrict__ coef, float *__restrict__ dgamma,
                                                             float *__restrict__ dbeta)
 {
-    __shared__ double tot[2 * 2048];
-    __shared__ double scratch[NT * 4];
-    sum_rows_to_lds<TIn>(rows, R, 2 * K, tot, scratch);
-    for (int k = threadIdx.x; k < K; k += NT) {
-        const double s1 = tot[k], s2 = tot[K + k];
+    __shared__ double red[COLSUM_NT * 8];
+    const int k0 = 4 * blockIdx.x;
+    colsum_pair4(rows, R, K, k0, red);
+    if (threadIdx.x < 4) {
+        const int k = k0 + threadIdx.x;
+        const double s1 = red[threadIdx.x], s2 = red[4 + threadIdx.x];
         dbeta[k] = (float)s1;
         dgamma[k] = (float)s2;
         coef[k] = gamma[k] * invstd[k];
@@ -167,7 +168,7 @@ int bnbwd_blocks(int M, int K)
 
 hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *mask,
                               const uint16_t *z, const float *gamma, const float *saved_mean,
-                              const float *saved_invstd, float *part, double *pp, float *coef,
+                              const float *saved_invstd, float *part, float *coef,
                               float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const int B = bnbwd_blocks((int)M, K);
@@ -178,14 +179,8 @@ hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *
     hipError_t e = launch(bnbwd_reduce_kernel, dim3(Bn), dim3(NT), 0, st, e0, nullptr, (const u32x4 *)dy, mask,
                           (const u32x4 *)z, saved_mean, saved_invstd, (int)M, K, rows, part);
     if (e != hipSuccess) return e;
-    if (Bn <= COLSUM_DIRECT_ROWS) {
-        e = launch(bnbwd_finalize_kernel<float>, dim3(1), dim3(NT), 0, st, nullptr, nullptr, (const float *)part, Bn,
-                   K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
-    } else {
-        if ((e = launch_colsum(part, Bn, 2 * K, pp, st)) != hipSuccess) return e;
-        e = launch(bnbwd_finalize_kernel<double>, dim3(1), dim3(NT), 0, st, nullptr, nullptr, (const double *)pp,
-                   colsum_groups(Bn), K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
-    }
+    e = launch(bnbwd_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, nullptr, nullptr, (const float *)part, Bn, K,
+               (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
     if (e != hipSuccess) return e;
     const int chunks = (int)(M * K / 8);
     const int cpr = K / 8;

@@ -6,30 +6,16 @@ namespace cbr {
 namespace {
 
 constexpr int NT = 256;
-constexpr int MAXK2 = 2 * 2048;
-
-// Stage 1 for many partial rows: block b folds rows [b*rpb, (b+1)*rpb) into pp[b][2K] (fp64).
-__global__ __launch_bounds__(NT) void colsum_stage1_kernel(const float *__restrict__ part, int R, int K2, int rpb,
-                                                           double *__restrict__ pp)
-{
-    __shared__ double tot[MAXK2];
-    __shared__ double scratch[NT * 4];
-    const int r0 = blockIdx.x * rpb;
-    const int rows = min(rpb, R - r0);
-    sum_rows_to_lds<float>(part + (size_t)r0 * K2, rows, K2, tot, scratch);
-    for (int k2 = threadIdx.x; k2 < K2; k2 += NT) pp[(size_t)blockIdx.x * K2 + k2] = tot[k2];
-}
 
 // The BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per channel:
 // mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the difference
 // accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
 // eq_bias = beta - gamma*mean*inv_std, and the running update
 // next = (1 - momentum)*prev + momentum*batch (BatchNorm CUDA page, section 2.4).
-// One block; the R partial rows ([R][2][K], sums then sums of squares) are summed
-// first.  rm_out/rv_out may alias rm_in/rv_in: each thread reads its channel before
-// writing it.
-template <typename TIn>
-__global__ __launch_bounds__(NT) void stats_finalize_kernel(const TIn *__restrict__ rows, int R, int K, double M,
+// Block b owns channels 4b..4b+3 and sums their columns of the R partial rows ([R][2][K],
+// sums then sums of squares).  rm_out/rv_out may alias rm_in/rv_in: each channel is
+// read before it is written, by the same thread.
+__global__ __launch_bounds__(NT) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
                                                             const float *__restrict__ gamma,
                                                             const float *__restrict__ beta, const float *rm_in,
                                                             const float *rv_in, float eps, float momentum,
@@ -38,12 +24,13 @@ __global__ __launch_bounds__(NT) void stats_finalize_kernel(const TIn *__restric
                                                             float *__restrict__ saved_invstd, float *rm_out,
                                                             float *rv_out)
 {
-    __shared__ double tot[MAXK2];
-    __shared__ double scratch[NT * 4];
-    sum_rows_to_lds<TIn>(rows, R, 2 * K, tot, scratch);
-    for (int k = threadIdx.x; k < K; k += NT) {
-        const double mean = tot[k] / M;
-        double var = tot[K + k] / M - mean * mean;
+    __shared__ double red[COLSUM_NT * 8];
+    const int k0 = 4 * blockIdx.x;
+    colsum_pair4(rows, R, K, k0, red);
+    if (threadIdx.x < 4) {
+        const int e = threadIdx.x, k = k0 + e;
+        const double mean = red[e] / M;
+        double var = red[4 + e] / M - mean * mean;
         if (!(var > 0.0)) var = 0.0;
         const double invstd = 1.0 / sqrt(var + (double)eps);
         const double gm = (double)gamma[k];
@@ -142,47 +129,21 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
     }
 }
 
-int colsum_rows_per_group(int R)
-{
-    const int G = std::min(COLSUM_MAX_GROUPS, R);
-    return (R + G - 1) / G;
-}
-
 }  // namespace
-
-int colsum_groups(int R)
-{
-    const int rpb = colsum_rows_per_group(R);
-    return (R + rpb - 1) / rpb;
-}
-
-hipError_t launch_colsum(const float *part, int R, int K2, double *pp, hipStream_t st, hipEvent_t e0)
-{
-    return launch(colsum_stage1_kernel, dim3(colsum_groups(R)), dim3(NT), 0, st, e0, nullptr, part, R, K2,
-                  colsum_rows_per_group(R), pp);
-}
 
 int train_partial_rows(const ConvGeom &g)
 {
     return halo_eligible(g) ? halo_grid(g) : conv_plan(g).tiles_m;
 }
 
-hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, double *pp,
-                                 const float *gamma, const float *beta, const float *rm_in,
-                                 const float *rv_in, float eps, float momentum, float *scale,
-                                 float *shift, float *saved_mean, float *saved_invstd,
-                                 float *rm_out, float *rv_out, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, const float *gamma,
+                                 const float *beta, const float *rm_in, const float *rv_in, float eps,
+                                 float momentum, float *scale, float *shift, float *saved_mean,
+                                 float *saved_invstd, float *rm_out, float *rv_out, hipStream_t st, hipEvent_t e0,
+                                 hipEvent_t e1)
 {
-    if (rows <= COLSUM_DIRECT_ROWS)
-        return launch(stats_finalize_kernel<float>, dim3(1), dim3(NT), 0, st, e0, e1, partials, rows, K, (double)M,
-                      gamma, beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out,
-                      rv_out);
-    const int G = colsum_groups(rows);
-    hipError_t e = launch_colsum(partials, rows, 2 * K, pp, st, e0);
-    if (e != hipSuccess) return e;
-    return launch(stats_finalize_kernel<double>, dim3(1), dim3(NT), 0, st, nullptr, e1, (const double *)pp, G, K,
-                  (double)M, gamma, beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out,
-                  rv_out);
+    return launch(stats_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, e0, e1, partials, rows, K, (double)M, gamma,
+                  beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out, rv_out);
 }
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,

@@ -55,16 +55,15 @@ ConvGeom dgrad_geom(const ConvGeom &g)
     return d;
 }
 
-struct TrainLayout { size_t partials, pp, scale, shift, total; };
+struct TrainLayout { size_t partials, scale, shift, total; };
 struct InferLayout { size_t wfold, bfold, total; };
-struct BwdLayout { size_t dz, part, pp, coef, wpart, wflip, total; };
+struct BwdLayout { size_t dz, part, coef, wpart, wflip, total; };
 
 TrainLayout train_layout(const ConvGeom &g)
 {
     TrainLayout L;
     size_t o = 0;
     L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)train_partial_rows(g));
-    L.pp = o; o = align_up(o + sizeof(double) * 2 * g.K * (size_t)COLSUM_MAX_GROUPS);
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
     L.total = o;
@@ -88,7 +87,6 @@ BwdLayout bwd_layout(const ConvGeom &g)
     size_t o = 0;
     L.dz = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.M * g.K);
     L.part = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)bnbwd_blocks(g.M, g.K));
-    L.pp = o; o = align_up(o + sizeof(double) * 2 * g.K * (size_t)COLSUM_MAX_GROUPS);
     L.coef = o; o = align_up(o + sizeof(float) * 3 * g.K);
     L.wpart = o; o = align_up(o + (wp.splits > 1 ? sizeof(float) * (size_t)wp.splits * g.K * g.Kg : 0));
     L.wflip = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.K * g.Kg);
@@ -180,7 +178,6 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
 
     hipStream_t s = (hipStream_t)stream;
     float *partials = (float *)ws_at(workspace, L.partials);
-    double *pp = (double *)ws_at(workspace, L.pp);
     float *scale = (float *)ws_at(workspace, L.scale);
     float *shift = (float *)ws_at(workspace, L.shift);
     // conv + channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
@@ -189,7 +186,7 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
                               : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
                                                   ev(events, 1));
     if (ec != hipSuccess) return CBR_E_HIP;
-    if (launch_stats_finalize(train_partial_rows(g), g.K, g.M, partials, pp, gamma, beta, run_mean_in, run_var_in,
+    if (launch_stats_finalize(train_partial_rows(g), g.K, g.M, partials, gamma, beta, run_mean_in, run_var_in,
                               eps, momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out, s,
                               ev(events, 2), ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
@@ -269,7 +266,7 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
     // WGrad is enqueued before DGrad on the same stream, so it has finished reading x
     // before DGrad may overwrite it when dx aliases x.
     if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
-                           (float *)ws_at(workspace, L.part), (double *)ws_at(workspace, L.pp),
+                           (float *)ws_at(workspace, L.part),
                            (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s, ev(events, 0),
                            ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;

@@ -53,13 +53,6 @@ hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const 
 // Rows of per-channel partial sums the training forward produces (one [2][K] row each).
 int train_partial_rows(const ConvGeom &g);
 
-// Column sums of a [R][2K] fp32 partial array are folded in two stages when R is large:
-// colsum_groups(R) <= 64 rows of fp64 partial sums, then the finalize kernel.
-constexpr int COLSUM_MAX_GROUPS = 64;
-constexpr int COLSUM_DIRECT_ROWS = 512;   // up to this many rows the finalize reads them directly
-int colsum_groups(int R);
-hipError_t launch_colsum(const float *part, int R, int K2, double *pp, hipStream_t st, hipEvent_t e0 = nullptr);
-
 // Blocks of the BN-backward reduction over M rows of K channels.
 int bnbwd_blocks(int M, int K);
 
@@ -75,11 +68,10 @@ hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, cons
                              const float *bias, uint16_t *out, float *partials, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, double *pp,
-                                 const float *gamma, const float *beta, const float *rm_in,
-                                 const float *rv_in, float eps, float momentum, float *scale,
-                                 float *shift, float *saved_mean, float *saved_invstd,
-                                 float *rm_out, float *rv_out, hipStream_t st,
+hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, const float *gamma,
+                                 const float *beta, const float *rm_in, const float *rv_in, float eps,
+                                 float momentum, float *scale, float *shift, float *saved_mean,
+                                 float *saved_invstd, float *rm_out, float *rv_out, hipStream_t st,
                                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,
@@ -93,7 +85,7 @@ hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, c
 
 hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *mask,
                               const uint16_t *z, const float *gamma, const float *saved_mean,
-                              const float *saved_invstd, float *part, double *pp, float *coef,
+                              const float *saved_invstd, float *part, float *coef,
                               float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st,
                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 

@@ -1,64 +1,57 @@
-// cbr_reduce.h -- block-wide column sums of a row-major [R][K2] array (float or double
-// rows), accumulated in fp64 in a fixed order, so results are reproducible bit for bit.
+// cbr_reduce.h -- per-channel column sums of a row-major [R][2K] float partials array
+// (row r: K sums, then K sums of a second quantity), accumulated in fp64 in a fixed
+// order, so results are reproducible bit for bit.
 #pragma once
 
 #include "cbr_common.h"
 
 namespace cbr {
 
-// All 256 threads of the block call this.  When the 16-byte column count of a row
-// divides 256, each thread owns one 16-byte column and a fixed set of rows, and issues
-// 16 independent loads before adding any of them (one memory latency per 16 rows of
-// its set, not one per row).  tot (LDS, K2 doubles) receives the sums; scratch (LDS)
-// needs 256 * 16 / sizeof(TIn) doubles.  Ends with a barrier.
-template <typename TIn>
-__device__ void sum_rows_to_lds(const TIn *__restrict__ in, int R, int K2, double *tot, double *scratch)
+constexpr int COLSUM_NT = 256;   // threads per block of the column-sum kernels
+
+// Called by all COLSUM_NT threads of a block that owns channels k0..k0+3 (k0 % 4 == 0).
+// Thread t sums rows t, t + 256, ... of columns k0..k0+3 and K+k0..K+k0+3 (eight 16-byte
+// loads in flight at a time), then a fixed halving tree over the threads combines them.
+// red (LDS) holds COLSUM_NT * 8 doubles; on return red[e] (e < 4) is the sum of column
+// k0 + e and red[4 + e] that of column K + k0 + e, visible to every thread.
+__device__ inline void colsum_pair4(const float *__restrict__ rows, int R, int K, int k0, double *red)
 {
-    constexpr int NTH = 256;
-    constexpr int VPL = 16 / (int)sizeof(TIn);
-    constexpr int UN = 16;
+    constexpr int UN = 8;
     const int tid = threadIdx.x;
-    const int cols = K2 / VPL;
-    if (K2 % VPL == 0 && cols <= NTH && NTH % cols == 0) {
-        const int col = tid % cols, rg = tid / cols, ngr = NTH / cols;
-        double acc[VPL];
+    double a[8];
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) acc[e] = 0.0;
-        for (int r0 = rg; r0 < R; r0 += ngr * UN) {
-            TIn v[UN][VPL];
+    for (int e = 0; e < 8; ++e) a[e] = 0.0;
+    for (int r0 = tid; r0 < R; r0 += COLSUM_NT * UN) {
+        f32x4 v[UN][2];
 #pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int r = r0 + u * ngr;
-                if (r < R) {
-                    const TIn *src = in + (size_t)r * K2 + col * VPL;
-#pragma unroll
-                    for (int e = 0; e < VPL; ++e) v[u][e] = src[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VPL; ++e) v[u][e] = (TIn)0;
-                }
+        for (int u = 0; u < UN; ++u) {
+            const int r = r0 + u * COLSUM_NT;
+            if (r < R) {
+                const float *row = rows + (size_t)r * 2 * K;
+                v[u][0] = *(const f32x4 *)(row + k0);
+                v[u][1] = *(const f32x4 *)(row + K + k0);
+            } else {
+                v[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                v[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int u = 0; u < UN; ++u)
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) acc[e] += (double)v[u][e];
         }
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) scratch[rg * K2 + col * VPL + e] = acc[e];
-        __syncthreads();
-        for (int k2 = tid; k2 < K2; k2 += NTH) {
-            double s = 0.0;
-            for (int g = 0; g < ngr; ++g) s += scratch[g * K2 + k2];
-            tot[k2] = s;
-        }
-    } else {
-        for (int k2 = tid; k2 < K2; k2 += NTH) {
-            double s = 0.0;
-            for (int r = 0; r < R; ++r) s += (double)in[(size_t)r * K2 + k2];
-            tot[k2] = s;
-        }
+        for (int u = 0; u < UN; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] += (double)v[u][0][e];
+                a[4 + e] += (double)v[u][1][e];
+            }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tid * 8 + e] = a[e];
     __syncthreads();
+    for (int s = COLSUM_NT / 2; s > 0; s >>= 1) {
+        if (tid < s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[tid * 8 + e] += red[(tid + s) * 8 + e];
+        __syncthreads();
+    }
 }
 
 }  // namespace cbr
