@@ -55,7 +55,7 @@ ConvGeom dgrad_geom(const ConvGeom &g)
     return d;
 }
 
-struct TrainLayout { size_t partials, scale, shift, total; };
+struct TrainLayout { size_t partials, scale, shift, wexp, total; };
 struct InferLayout { size_t wfold, bfold, total; };
 struct BwdLayout { size_t dz, part, coef, wpart, wflip, total; };
 
@@ -66,6 +66,7 @@ TrainLayout train_layout(const ConvGeom &g)
     L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)train_partial_rows(g));
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
+    L.wexp = o; o = align_up(o + (c3s2_eligible(g) ? c3s2_wexp_bytes(g) : 0));
     L.total = o;
     return L;
 }
@@ -181,10 +182,12 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
     float *scale = (float *)ws_at(workspace, L.scale);
     float *shift = (float *)ws_at(workspace, L.shift);
     // conv + channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
-    const hipError_t ec = halo_eligible(g)
-                              ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
-                              : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
-                                                  ev(events, 1));
+    const hipError_t ec =
+        halo_eligible(g)   ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
+        : c3s2_eligible(g) ? launch_conv_c3s2_stats(g, x, w, (uint16_t *)ws_at(workspace, L.wexp), z, partials, s,
+                                                    ev(events, 0), ev(events, 1))
+                           : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
+                                               ev(events, 1));
     if (ec != hipSuccess) return CBR_E_HIP;
     if (launch_stats_finalize(train_partial_rows(g), g.K, g.M, partials, gamma, beta, run_mean_in, run_var_in,
                               eps, momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out, s,

@@ -50,6 +50,15 @@ size_t halo_lds_bytes(const ConvGeom &g);
 hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
                                     float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 
+// First-layer conv (3 input channels, stride 2, 64 output channels) + channel statistics:
+// pixels widened to 4 channels in LDS; the filter widened to [64][R][8][4] in workspace.
+bool c3s2_eligible(const ConvGeom &g);
+int c3s2_grid(const ConvGeom &g);
+size_t c3s2_lds_bytes(const ConvGeom &g);
+size_t c3s2_wexp_bytes(const ConvGeom &g);
+hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *wexp,
+                                  uint16_t *z, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+
 // Rows of per-channel partial sums the training forward produces (one [2][K] row each).
 int train_partial_rows(const ConvGeom &g);
 

@@ -63,6 +63,26 @@ def test_train_forward_persistent_3x3(g):
     H.check_train(g, d, res, ora)
 
 
+# The first-layer kernel (3 input channels, stride 2, 64 output channels, W % 8 == 0,
+# odd padding): several bands, a partial last band, short and narrow images, 3x3 and
+# 5x5 filters.
+FIRST_LAYER_GEOMS = [
+    Geometry(2, 32, 32, 3, 64, 7, 7, 2, 3),
+    Geometry(1, 24, 40, 3, 64, 7, 7, 2, 3),
+    Geometry(3, 17, 16, 3, 64, 3, 3, 2, 1),      # 9 output rows: partial last band
+    Geometry(2, 40, 8, 3, 64, 5, 5, 2, 1),       # 3 output columns
+]
+
+
+@pytest.mark.parametrize("g", FIRST_LAYER_GEOMS, ids=str)
+def test_train_forward_first_layer(g):
+    H.log(f"train fwd (first layer) {g}")
+    d = draw(g, "train", 15)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
 @pytest.mark.parametrize("g", INFER_GEOMS, ids=str)
 def test_infer_small(g):
     H.log(f"infer {g}")
