@@ -29,7 +29,7 @@ int make_geom(const cbr_shape *s, ConvGeom *g)
     const long P = hp / s->stride_h + 1, Q = wp / s->stride_w + 1;
     if (s->k % 8 != 0 || s->k > 2048) return CBR_E_UNSUPPORTED;
     if (s->pad_h >= s->r || s->pad_w >= s->s) return CBR_E_UNSUPPORTED;
-    const double lim = 2147483647.0;
+    const double lim = 1073741823.0;   // < 2^30 elements: every byte offset fits 31 bits
     if ((double)s->n * s->h * s->w * s->c > lim || (double)s->k * s->r * s->s * s->c > lim ||
         (double)s->n * P * Q * s->k > lim)
         return CBR_E_UNSUPPORTED;

@@ -4,8 +4,10 @@
 // over kk = (r,s,c) with c fastest (KRSC filter rows are contiguous in kk).  A workgroup
 // of four wave64s computes a BM x BN tile; each K-step stages a BM x 64 slice of the
 // implicit im2col matrix and a BN x 64 slice of the filter through LDS (double
-// buffered, 16-byte rows padded to 144 bytes so the fragment reads are conflict-free)
-// and runs v_mfma_f32_16x16x32_bf16 with fp32 accumulators.
+// buffered, rows padded to 144 bytes so the fragment reads are conflict-free) and runs
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  The global loads of a K-step are
+// issued two K-steps ahead (two register stages), so their latency is covered by two
+// K-steps of MFMAs of this workgroup and of the other workgroup sharing the CU.
 //
 // Epilogues (one template parameter):
 //   EPI_STATS      store z as bf16 and, from the fp32 accumulators, the per-channel
@@ -35,11 +37,28 @@ struct ConvParams {
     float *partials;
 };
 
-template <int BM, int BN, bool VEC, int EPI>
-__global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Gather modes of the implicit im2col rows.
+//   GATHER_SCALAR  C % 8 != 0: element loads (first layers that no special kernel takes);
+//   GATHER_VEC     C % 8 == 0: 16-byte loads, each thread decodes its own tap;
+//   GATHER_TAP     C % 64 == 0: a K-step lies inside one filter tap, so the tap and its
+//                  offset are uniform and each thread adds them to a per-row base.
+// The vector modes load through bounds-checked buffer resources: a padding position
+// or a row past M gets an offset past the end and reads zeros, with no branch.
+enum { GATHER_SCALAR = 0, GATHER_VEC = 1, GATHER_TAP = 2 };
+constexpr uint32_t OOB = 0x80000000u;   // past the end of every buffer (sizes < 2^31)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int BN, int MODE, int EPI>
+__global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
 {
     constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int MI = WM / 16, NJ = WN / 16;
+    constexpr int MI = WM / 32, NJ = WN / 32;
     constexpr int GPR = BK / 8;             // 16-byte groups per staged row
     constexpr int RPP = NT / GPR;           // rows covered per load pass
     constexpr int AI = BM / RPP, BI = BN / RPP;
@@ -61,6 +80,7 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
     const int rbase = tid / GPR;
     const int PQ = g.P * g.Q;
 
+    constexpr bool VEC = MODE != GATHER_SCALAR;
     int a_hb[AI], a_wb[AI], a_nb[AI];
 #pragma unroll
     for (int j = 0; j < AI; ++j) {
@@ -72,14 +92,40 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
             a_wb[j] = q * g.sw - g.pw;
             a_nb[j] = n * g.H * g.W * g.C;
         } else {
-            a_hb[j] = 0; a_wb[j] = 0; a_nb[j] = -1;
+            a_hb[j] = -0x40000000; a_wb[j] = 0; a_nb[j] = -1;   // never inside the image
         }
     }
+    const __amdgpu_buffer_rsrc_t xr = rsrc_of(x, (uint32_t)((size_t)g.N * g.H * g.W * g.C * 2));
+    const __amdgpu_buffer_rsrc_t wr = rsrc_of(wt, (uint32_t)((size_t)g.K * g.Kg * 2));
+    // Byte offset of each A row's pixel (tap 0, channel grp*8) and each B row's start.
+    int a_off[AI], b_off[AI > BI ? AI : BI];
+#pragma unroll
+    for (int j = 0; j < AI; ++j) a_off[j] = a_nb[j] >= 0 ? 2 * (a_nb[j] + (a_hb[j] * g.W + a_wb[j]) * g.C + grp * 8) : 0;
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int k = n0 + rbase + RPP * j;
+        b_off[j] = k < g.K ? 2 * (k * g.Kg + grp * 8) : (int)OOB;
+    }
 
-    u32x4 ra[AI], rb[BI];
-    auto load = [&](int ks) {
+    u32x4 ra2[2][AI], rb2[2][BI];
+    auto load = [&](int ks, u32x4 (&ra)[AI], u32x4 (&rb)[BI]) {
         const int kk0 = ks * BK + grp * 8;
-        if constexpr (VEC) {
+        if constexpr (MODE == GATHER_TAP) {
+            // Uniform tap (r, s) and channel base of this K-step.
+            const int kb = ks * BK;
+            const int tap = kb / g.C, c0b = kb - tap * g.C;
+            const int r = tap / g.S, s = tap - r * g.S;
+            const int toff = 2 * ((r * g.W + s) * g.C + c0b);
+#pragma unroll
+            for (int j = 0; j < AI; ++j) {
+                const int h = a_hb[j] + r, w = a_wb[j] + s;
+                const bool ok = (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+                ra[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? a_off[j] + toff : (int)OOB, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < BI; ++j)
+                rb[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, b_off[j] < 0 ? (int)OOB : b_off[j] + 2 * kb, 0, 0);
+        } else if constexpr (VEC) {
             int r = 0, s = 0, c0 = 0;
             const bool kok = kk0 < g.Kg;
             if (kok) {
@@ -88,18 +134,17 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
                 r = tap / g.S;
                 s = tap - r * g.S;
             }
+            const int toff = 2 * ((r * g.W + s) * g.C + c0 - grp * 8);
 #pragma unroll
             for (int j = 0; j < AI; ++j) {
                 const int h = a_hb[j] + r, w = a_wb[j] + s;
-                const bool ok = kok && a_nb[j] >= 0 && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-                ra[j] = ok ? *(const u32x4 *)(x + a_nb[j] + (h * g.W + w) * g.C + c0) : u32x4{0, 0, 0, 0};
+                const bool ok = kok && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+                ra[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? a_off[j] + toff : (int)OOB, 0, 0);
             }
 #pragma unroll
-            for (int j = 0; j < BI; ++j) {
-                const int k = n0 + rbase + RPP * j;
-                const bool ok = kok && k < g.K;
-                rb[j] = ok ? *(const u32x4 *)(wt + (size_t)k * g.Kg + kk0) : u32x4{0, 0, 0, 0};
-            }
+            for (int j = 0; j < BI; ++j)
+                rb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, (kok && b_off[j] >= 0) ? b_off[j] + 2 * ks * BK : (int)OOB, 0, 0);
         } else {
             int er[8], es[8], ec[8];
             bool eok[8];
@@ -135,7 +180,7 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
             }
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const u32x4 (&ra)[AI], const u32x4 (&rb)[BI]) {
         uint16_t *sa = smem + buf * STAGE;
         uint16_t *sb = sa + BM * LDK;
 #pragma unroll
@@ -144,46 +189,65 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
         for (int j = 0; j < BI; ++j) *(u32x4 *)(sb + (rbase + RPP * j) * LDK + grp * 8) = rb[j];
     };
 
-    f32x4 acc[MI][NJ];
+    f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+    // 32x32x16 fragments: lane l reads row (l & 31), reduction elements 8*(l >> 5)..+7
+    // of the 16-element slice kh.
+    // Fragments of slice kh + 1 are read while the MFMAs of slice kh run.
     auto compute = [&](int buf) {
         const uint16_t *sa = smem + buf * STAGE;
         const uint16_t *sb = sa + BM * LDK;
-#pragma unroll
-        for (int kh = 0; kh < BK / 32; ++kh) {
-            bf16x8 a[MI], b[NJ];
+        bf16x8 a[2][MI], b[2][NJ];
+        auto rd = [&](int kh, int d) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                a[i] = *(const bf16x8 *)(sa + (wm * WM + 16 * i + (lane & 15)) * LDK + kh * 32 + (lane >> 4) * 8);
+                a[d][i] = *(const bf16x8 *)(sa + (wm * WM + 32 * i + (lane & 31)) * LDK + kh * 16 + (lane >> 5) * 8);
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                b[j] = *(const bf16x8 *)(sb + (wn * WN + 16 * j + (lane & 15)) * LDK + kh * 32 + (lane >> 4) * 8);
+                b[d][j] = *(const bf16x8 *)(sb + (wn * WN + 32 * j + (lane & 31)) * LDK + kh * 16 + (lane >> 5) * 8);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int kh = 0; kh < BK / 16; ++kh) {
+            if (kh + 1 < BK / 16) rd(kh + 1, (kh + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kh & 1][i], b[kh & 1][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // Stage ks lives in LDS buffer ks & 1 while it is computed; stage ks + 1 is in the
+    // register set (ks + 1) & 1, loaded during K-step ks - 1; stage ks + 2 is loaded
+    // into register set ks & 1 (free since stage ks went to LDS).
     const int ksteps = (g.Kg + BK - 1) / BK;
-    load(0);
-    store(0);
+    load(0, ra2[0], rb2[0]);
+    if (ksteps > 1) load(1, ra2[1], rb2[1]);
+    store(0, ra2[0], rb2[0]);
     __syncthreads();
-    for (int ks = 0; ks < ksteps; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < ksteps) load(ks + 1);
-        compute(cur);
-        if (ks + 1 < ksteps) store(cur ^ 1);
+    for (int ks = 0; ks < ksteps; ks += 2) {
+        if (ks + 2 < ksteps) load(ks + 2, ra2[0], rb2[0]);
+        compute(0);
+        if (ks + 1 < ksteps) store(1, ra2[1], rb2[1]);
+        __syncthreads();
+        if (ks + 1 >= ksteps) break;
+        if (ks + 3 < ksteps) load(ks + 3, ra2[1], rb2[1]);
+        compute(1);
+        if (ks + 2 < ksteps) store(0, ra2[0], rb2[0]);
         __syncthreads();
     }
 
-    // Epilogue.  Accumulator layout of v_mfma_f32_16x16x32: lane l holds column
-    // (l & 15) and rows 4*(l >> 4) + v, v = 0..3, of each 16 x 16 block.
+    // Epilogue.  Accumulator layout of v_mfma_f32_32x32x16: lane l holds column
+    // (l & 31) and rows 8*(v/4) + 4*(l >> 5) + v%4, v = 0..15, of each 32 x 32 block.
     if constexpr (EPI == EPI_STATS) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -191,25 +255,23 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
+                for (int v = 0; v < 16; ++v) {
                     const float a = acc[i][j][v];
                     s1 += a;
                     s2 += a * a;
                 }
-            s1 += __shfl_xor(s1, 16);
-            s2 += __shfl_xor(s2, 16);
             s1 += __shfl_xor(s1, 32);
             s2 += __shfl_xor(s2, 32);
-            if (lane < 16) {
-                sstat[wm][0][wn * WN + 16 * j + lane] = s1;
-                sstat[wm][1][wn * WN + 16 * j + lane] = s2;
+            if (lane < 32) {
+                sstat[wm][0][wn * WN + 32 * j + lane] = s1;
+                sstat[wm][1][wn * WN + 32 * j + lane] = s2;
             }
         }
     }
     float bcol[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int col = n0 + wn * WN + 16 * j + (lane & 15);
+        const int col = n0 + wn * WN + 32 * j + (lane & 31);
         bcol[j] = (EPI == EPI_BIAS_RELU && col < g.K) ? prm.bias[col] : 0.f;
     }
     uint16_t *so = smem;
@@ -218,9 +280,9 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = wm * WM + 16 * i + 4 * (lane >> 4) + v;
-                const int col = wn * WN + 16 * j + (lane & 15);
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int col = wn * WN + 32 * j + (lane & 31);
                 float val = acc[i][j][v];
                 if constexpr (EPI == EPI_BIAS_RELU) val = fmaxf(val + bcol[j], 0.f);
                 so[row * LDO + col] = (uint16_t)f32_to_bf16_bits(val);
@@ -246,15 +308,24 @@ __global__ __launch_bounds__(NT) void conv_fprop_kernel(ConvParams prm)
     }
 }
 
-template <int BM, int BN, bool VEC>
+template <int BM, int BN, int MODE>
 hipError_t launch_epi(int epi, const ConvParams &prm, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     switch (epi) {
-    case EPI_STATS: return launch(conv_fprop_kernel<BM, BN, VEC, EPI_STATS>, grid, dim3(NT), 0, st, e0, e1, prm);
+    case EPI_STATS: return launch(conv_fprop_kernel<BM, BN, MODE, EPI_STATS>, grid, dim3(NT), 0, st, e0, e1, prm);
     case EPI_BIAS_RELU:
-        return launch(conv_fprop_kernel<BM, BN, VEC, EPI_BIAS_RELU>, grid, dim3(NT), 0, st, e0, e1, prm);
-    default: return launch(conv_fprop_kernel<BM, BN, VEC, EPI_PLAIN>, grid, dim3(NT), 0, st, e0, e1, prm);
+        return launch(conv_fprop_kernel<BM, BN, MODE, EPI_BIAS_RELU>, grid, dim3(NT), 0, st, e0, e1, prm);
+    default: return launch(conv_fprop_kernel<BM, BN, MODE, EPI_PLAIN>, grid, dim3(NT), 0, st, e0, e1, prm);
     }
+}
+
+template <int BM, int BN>
+hipError_t launch_mode(const ConvGeom &g, int epi, const ConvParams &prm, dim3 grid, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1)
+{
+    if (g.C % 64 == 0) return launch_epi<BM, BN, GATHER_TAP>(epi, prm, grid, st, e0, e1);
+    if (g.C % 8 == 0) return launch_epi<BM, BN, GATHER_VEC>(epi, prm, grid, st, e0, e1);
+    return launch_epi<BM, BN, GATHER_SCALAR>(epi, prm, grid, st, e0, e1);
 }
 
 }  // namespace
@@ -277,12 +348,8 @@ hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, cons
     const ConvPlan p = conv_plan(g);
     ConvParams prm{g, x, w, bias, out, partials};
     dim3 grid(p.tiles_m, p.tiles_n);
-    if (p.bn == 128) {
-        return p.vec ? launch_epi<128, 128, true>(epi, prm, grid, st, e0, e1)
-                     : launch_epi<128, 128, false>(epi, prm, grid, st, e0, e1);
-    }
-    return p.vec ? launch_epi<128, 64, true>(epi, prm, grid, st, e0, e1)
-                 : launch_epi<128, 64, false>(epi, prm, grid, st, e0, e1);
+    if (p.bn == 128) return launch_mode<128, 128>(g, epi, prm, grid, st, e0, e1);
+    return launch_mode<128, 64>(g, epi, prm, grid, st, e0, e1);
 }
 
 }  // namespace cbr

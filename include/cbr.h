@@ -34,7 +34,7 @@
  * aborts or exits the process.
  *
  * Limits (CBR_E_UNSUPPORTED): K % 8 != 0 ([CBR] section 8: output channels a multiple
- * of 8); K > 2048; any tensor with 2^31 elements or more; pad >= filter size;
+ * of 8); K > 2048; any tensor with 2^30 elements or more; pad >= filter size;
  * dx requested with a stride other than 1.
  */
 #ifndef CBR_H

@@ -62,6 +62,7 @@ def test_output_hw_and_mask_words(lib):
     (dict(k=12), 3), (dict(k=4096), 3),          # K % 8, K > 2048
     (dict(pad=3), 3),                            # pad >= filter size
     (dict(n=70000, h=200, w=200, c=64), 3),      # tensor of 2^31 elements or more
+    (dict(n=300, h=256, w=256, c=64), 3),        # 2^30 elements or more (byte offsets need 31 bits)
 ])
 def test_shape_validation(lib, kw, status):
     with pytest.raises(cbr.CbrError) as e:
