@@ -19,6 +19,26 @@ namespace {
 constexpr int NT = 256;
 constexpr int BKM = 64;        // output pixels per K-step
 constexpr int LDK = BKM + 8;   // LDS row stride (elements)
+constexpr int WGRAD_STAGES_128 = 1;   // register stages of the 128 x 128 tile
+
+// Unsigned division by a fixed divisor d >= 1 for dividends below 2^31 (round-up
+// multiplier method): n / d == (umulhi(n, mul) + n) >> shift.
+struct FastDiv {
+    uint32_t mul, shift;
+};
+
+FastDiv fast_div(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t div_by(uint32_t n, FastDiv f)
+{
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
 
 struct WgradParams {
     ConvGeom g;
@@ -26,6 +46,7 @@ struct WgradParams {
     const uint16_t *x;
     float *out;            // [splits][K][Kg] (or dw itself when splits == 1)
     int rows_per_split;
+    FastDiv dpq, dq;       // division by P*Q and by Q
 };
 
 __device__ __forceinline__ int swz(int row, int m)   // element offset of (row, m) in a tile row
@@ -33,11 +54,20 @@ __device__ __forceinline__ int swz(int row, int m)   // element offset of (row, 
     return row * LDK + ((((m >> 3) ^ (row >> 3)) & 7) << 3) + (m & 7);
 }
 
-template <int BMK, int BNC, bool VEC>
-__global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
+constexpr uint32_t OOB = 0x80000000u;   // past the end of every buffer (sizes < 2^31)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BMK, int BNC, bool VEC, int STAGES>
+__global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
 {
     constexpr int WM = BMK / 2, WN = BNC / 2;
-    constexpr int MI = WM / 16, NJ = WN / 16;
+    constexpr int MI = WM / 32, NJ = WN / 32;
     constexpr int AI = (BKM / 2) * (BMK / 8) / NT;   // (pixel pair, chunk) items per thread
     constexpr int BI = (BKM / 2) * (BNC / 8) / NT;
     constexpr int STAGE = (BMK + BNC) * LDK;
@@ -45,14 +75,14 @@ __global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
     const ConvGeom &g = prm.g;
-    const uint16_t *__restrict__ dz = prm.dz;
     const uint16_t *__restrict__ x = prm.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int k0 = blockIdx.y * BMK, n0 = blockIdx.x * BNC;
     const int mbeg = blockIdx.z * prm.rows_per_split;
     const int mend = min(g.M, mbeg + prm.rows_per_split);
-    const int PQ = g.P * g.Q;
+    const __amdgpu_buffer_rsrc_t dzr = rsrc_of(prm.dz, (uint32_t)((size_t)g.M * g.K * 2));
+    const __amdgpu_buffer_rsrc_t xr = rsrc_of(x, (uint32_t)((size_t)g.N * g.H * g.W * g.C * 2));
 
     // item i -> (pixel pair p, chunk cc): within a wave, 8 pairs x 8 chunks.
     auto item_p = [](int i) { return (i & 7) + 8 * ((i >> 6) & 3); };
@@ -71,8 +101,7 @@ __global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
         b_s[j] = tap - b_r[j] * g.S;
     }
 
-    u32x4 ra[AI][2], rb[BI][2];
-    auto load = [&](int mstep) {
+    auto load = [&](int mstep, u32x4 (&ra)[AI][2], u32x4 (&rb)[BI][2]) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int it = tid + NT * j;
@@ -80,7 +109,8 @@ __global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int m = mstep + 2 * item_p(it) + h;
-                ra[j][h] = (m < mend && k < g.K) ? *(const u32x4 *)(dz + (size_t)m * g.K + k) : u32x4{0, 0, 0, 0};
+                const bool ok = m < mend && k < g.K;
+                ra[j][h] = __builtin_amdgcn_raw_buffer_load_b128(dzr, ok ? 2 * (m * g.K + k) : (int)OOB, 0, 0);
             }
         }
 #pragma unroll
@@ -89,42 +119,39 @@ __global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int m = mstep + 2 * item_p(it) + h;
-                u32x4 v = u32x4{0, 0, 0, 0};
-                if (m < mend && b_ok[j]) {
-                    const int n = m / PQ, rem = m - n * PQ;
-                    const int p = rem / g.Q, q = rem - p * g.Q;
-                    const int hb = p * g.sh - g.ph, wb = q * g.sw - g.pw;
-                    const uint16_t *xn = x + (size_t)n * g.H * g.W * g.C;
-                    if constexpr (VEC) {
-                        const int hh = hb + b_r[j], ww = wb + b_s[j];
-                        if ((unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W)
-                            v = *(const u32x4 *)(xn + (hh * g.W + ww) * g.C + b_c[j]);
-                    } else {
-                        const int kk0 = n0 + 8 * item_c(it);
-                        uint32_t e16[8];
+                const int n = (int)div_by((uint32_t)m, prm.dpq), rem = m - n * g.P * g.Q;
+                const int p = (int)div_by((uint32_t)rem, prm.dq), q = rem - p * g.Q;
+                const int hb = p * g.sh - g.ph, wb = q * g.sw - g.pw;
+                const int nb = n * g.H * g.W * g.C;
+                if constexpr (VEC) {
+                    const int hh = hb + b_r[j], ww = wb + b_s[j];
+                    const bool ok = m < mend && b_ok[j] && (unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W;
+                    rb[j][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                        xr, ok ? 2 * (nb + (hh * g.W + ww) * g.C + b_c[j]) : (int)OOB, 0, 0);
+                } else {
+                    const int kk0 = n0 + 8 * item_c(it);
+                    uint32_t e16[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int kk = kk0 + e;
-                            e16[e] = 0u;
-                            if (kk < g.Kg) {
-                                const int tap = kk / g.C, c = kk - tap * g.C;
-                                const int r = tap / g.S, s = tap - r * g.S;
-                                const int hh = hb + r, ww = wb + s;
-                                if ((unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W)
-                                    e16[e] = xn[(hh * g.W + ww) * g.C + c];
-                            }
+                    for (int e = 0; e < 8; ++e) {
+                        const int kk = kk0 + e;
+                        e16[e] = 0u;
+                        if (m < mend && kk < g.Kg) {
+                            const int tap = kk / g.C, c = kk - tap * g.C;
+                            const int r = tap / g.S, s = tap - r * g.S;
+                            const int hh = hb + r, ww = wb + s;
+                            if ((unsigned)hh < (unsigned)g.H && (unsigned)ww < (unsigned)g.W)
+                                e16[e] = x[nb + (hh * g.W + ww) * g.C + c];
                         }
-                        v = u32x4{e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
-                                  e16[6] | (e16[7] << 16)};
                     }
+                    rb[j][h] = u32x4{e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
+                                     e16[6] | (e16[7] << 16)};
                 }
-                rb[j][h] = v;
             }
         }
     };
     // Transposed store: channel-chunk element e of pixels (2p, 2p+1) -> row 8*cc + e,
     // columns 2p and 2p+1 (one 32-bit LDS write).
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const u32x4 (&ra)[AI][2], const u32x4 (&rb)[BI][2]) {
         uint16_t *sa = smem + buf * STAGE;
         uint16_t *sb = sa + BMK * LDK;
 #pragma unroll
@@ -149,54 +176,90 @@ __global__ __launch_bounds__(NT) void conv_wgrad_kernel(WgradParams prm)
         }
     };
 
-    f32x4 acc[MI][NJ];
+    f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+    // 32x32x16 fragments: lane l reads row (l & 31), pixels 8*(l >> 5)..+7 of slice kh;
+    // the fragments of slice kh + 1 are read while the MFMAs of slice kh run.
     auto compute = [&](int buf) {
         const uint16_t *sa = smem + buf * STAGE;
         const uint16_t *sb = sa + BMK * LDK;
+        bf16x8 a[2][MI], b[2][NJ];
+        auto rd = [&](int kh, int d) {
+            const int mb = kh * 16 + (lane >> 5) * 8;
 #pragma unroll
-        for (int kh = 0; kh < BKM / 32; ++kh) {
-            const int mb = kh * 32 + (lane >> 4) * 8;
-            bf16x8 a[MI], b[NJ];
+            for (int i = 0; i < MI; ++i) a[d][i] = *(const bf16x8 *)(sa + swz(wm * WM + 32 * i + (lane & 31), mb));
 #pragma unroll
-            for (int i = 0; i < MI; ++i) a[i] = *(const bf16x8 *)(sa + swz(wm * WM + 16 * i + (lane & 15), mb));
+            for (int j = 0; j < NJ; ++j) b[d][j] = *(const bf16x8 *)(sb + swz(wn * WN + 32 * j + (lane & 31), mb));
+        };
+        rd(0, 0);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) b[j] = *(const bf16x8 *)(sb + swz(wn * WN + 16 * j + (lane & 15), mb));
+        for (int kh = 0; kh < BKM / 16; ++kh) {
+            if (kh + 1 < BKM / 16) rd(kh + 1, (kh + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kh & 1][i], b[kh & 1][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     const int nsteps = (mend - mbeg + BKM - 1) / BKM;
-    if (nsteps > 0) {
-        load(mbeg);
-        store(0);
-    }
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int cur = st & 1;
-        if (st + 1 < nsteps) load(mbeg + (st + 1) * BKM);
-        compute(cur);
-        if (st + 1 < nsteps) store(cur ^ 1);
+    if constexpr (STAGES == 2) {
+        // Two register stages: the loads of a K-step are issued two K-steps ahead.
+        u32x4 ra2[2][AI][2], rb2[2][BI][2];
+        if (nsteps > 0) {
+            load(mbeg, ra2[0], rb2[0]);
+            if (nsteps > 1) load(mbeg + BKM, ra2[1], rb2[1]);
+            store(0, ra2[0], rb2[0]);
+        }
         __syncthreads();
+        for (int st = 0; st < nsteps; st += 2) {
+            if (st + 2 < nsteps) load(mbeg + (st + 2) * BKM, ra2[0], rb2[0]);
+            compute(0);
+            if (st + 1 < nsteps) store(1, ra2[1], rb2[1]);
+            __syncthreads();
+            if (st + 1 >= nsteps) break;
+            if (st + 3 < nsteps) load(mbeg + (st + 3) * BKM, ra2[1], rb2[1]);
+            compute(1);
+            if (st + 2 < nsteps) store(0, ra2[0], rb2[0]);
+            __syncthreads();
+        }
+    } else {
+        // One register stage: the loads of a K-step are issued one K-step ahead.
+        u32x4 ra[AI][2], rb[BI][2];
+        if (nsteps > 0) {
+            load(mbeg, ra, rb);
+            store(0, ra, rb);
+        }
+        __syncthreads();
+        for (int st = 0; st < nsteps; ++st) {
+            const int cur = st & 1;
+            if (st + 1 < nsteps) load(mbeg + (st + 1) * BKM, ra, rb);
+            compute(cur);
+            if (st + 1 < nsteps) store(cur ^ 1, ra, rb);
+            __syncthreads();
+        }
     }
 
+    // Accumulator layout of v_mfma_f32_32x32x16: lane l holds column (l & 31) and rows
+    // 8*(v/4) + 4*(l >> 5) + v%4 of each 32 x 32 block.
     float *out = prm.out + (size_t)blockIdx.z * g.K * g.Kg;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int k = k0 + wm * WM + 16 * i + 4 * (lane >> 4) + v;
-                const int kk = n0 + wn * WN + 16 * j + (lane & 15);
+            for (int v = 0; v < 16; ++v) {
+                const int k = k0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int kk = n0 + wn * WN + 32 * j + (lane & 31);
                 if (k < g.K && kk < g.Kg) out[(size_t)k * g.Kg + kk] = acc[i][j][v];
             }
 }
@@ -251,17 +314,18 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16
                              hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const WgradPlan p = wgrad_plan(g.M, g.K, g.Kg);
-    WgradParams prm{g, dz, x, p.splits == 1 ? dw : part, p.rows_per_split};
+    WgradParams prm{g, dz, x, p.splits == 1 ? dw : part, p.rows_per_split, fast_div((uint32_t)(g.P * g.Q)),
+                    fast_div((uint32_t)g.Q)};
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
     const bool vec = (g.C % 8) == 0;
     const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;   // end event on the last kernel of the stage
     hipError_t e;
     if (p.bm == 128)
-        e = vec ? launch(conv_wgrad_kernel<128, 128, true>, grid, dim3(NT), 0, st, e0, ek, prm)
-                : launch(conv_wgrad_kernel<128, 128, false>, grid, dim3(NT), 0, st, e0, ek, prm);
+        e = vec ? launch(conv_wgrad_kernel<128, 128, true, WGRAD_STAGES_128>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<128, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
     else
-        e = vec ? launch(conv_wgrad_kernel<64, 128, true>, grid, dim3(NT), 0, st, e0, ek, prm)
-                : launch(conv_wgrad_kernel<64, 128, false>, grid, dim3(NT), 0, st, e0, ek, prm);
+        e = vec ? launch(conv_wgrad_kernel<64, 128, true, 2>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<64, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
     if (e != hipSuccess || p.splits == 1) return e;
     const long n = (long)g.K * g.Kg;
     const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);
