@@ -43,7 +43,7 @@ ConvPlan conv_plan(const ConvGeom &g);
 
 // Persistent 3x3 / stride 1 / pad 1, 64 -> 64 channel convolution + channel statistics.
 constexpr int HALO_MAX_GRID = 256;                        // one workgroup per MI355X CU
-constexpr int HALO_MAX_LDS = 64 * 1168 + 10 * (56 + 2) * 144;  // filter + input-row ring, W <= 56
+constexpr int HALO_MAX_LDS = 64 * 1168 + 10 * (56 + 2) * 128;  // filter + input-row ring, W <= 56
 bool halo_eligible(const ConvGeom &g);
 int halo_grid(const ConvGeom &g);
 size_t halo_lds_bytes(const ConvGeom &g);

@@ -42,15 +42,20 @@ def test_train_forward_small(g):
     H.check_train(g, d, res, ora)
 
 
-# The persistent 3x3 / 64-channel kernel: partial last steps, several images per
-# workgroup (N > 256), short and narrow images.
+# The persistent 3x3 / 64-channel kernel (W a multiple of 8, 8..56): partial last steps,
+# several images per workgroup (N > 256), short and narrow images, partial pixel blocks.
+# The 64-channel 3x3 shapes it does not take (W % 8 != 0) run the generic conv.
 HALO_GEOMS = [
-    Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1),     # 8 + 4 output rows
-    Geometry(3, 9, 20, 64, 64, 3, 3, 1, 1),      # 160-pixel steps (5 blocks)
-    Geometry(1, 56, 56, 64, 64, 3, 3, 1, 1),     # one full image, seven steps
-    Geometry(300, 5, 7, 64, 64, 3, 3, 1, 1),     # two images for some workgroups, partial blocks
+    Geometry(2, 12, 16, 64, 64, 3, 3, 1, 1),     # three 4-row steps of 2 blocks
+    Geometry(3, 9, 24, 64, 64, 3, 3, 1, 1),      # 96-pixel steps, a one-row last step
+    Geometry(1, 56, 56, 64, 64, 3, 3, 1, 1),     # one full image, fourteen steps
+    Geometry(300, 5, 8, 64, 64, 3, 3, 1, 1),     # two images for some workgroups
     Geometry(2, 3, 56, 64, 64, 3, 3, 1, 1),      # fewer rows than a step
-    Geometry(2, 17, 2, 64, 64, 3, 3, 1, 1),      # the narrowest image
+    Geometry(2, 17, 8, 64, 64, 3, 3, 1, 1),      # the narrowest image: one block per step
+    Geometry(1, 6, 40, 64, 64, 3, 3, 1, 1),      # 5 blocks per step
+    Geometry(2, 7, 48, 64, 64, 3, 3, 1, 1),      # a 3-row last step of 4.5 blocks
+    Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1),     # generic conv (W % 8 != 0)
+    Geometry(300, 5, 7, 64, 64, 3, 3, 1, 1),     # generic conv, N > 256
 ]
 
 
@@ -148,7 +153,7 @@ def test_running_stats_in_place():
 
 
 def test_bitwise_deterministic():
-    g = Geometry(8, 20, 20, 64, 64, 3, 3, 1, 1)
+    g = Geometry(8, 20, 24, 64, 64, 3, 3, 1, 1)
     d = draw(g, "bwd", 13)
     r1, dv1 = H.gpu_train(g, d)
     r2, dv2 = H.gpu_train(g, d)
@@ -205,7 +210,7 @@ def test_backward_full_workload():
 
 
 @pytest.mark.parametrize("g", [Geometry(2, 6, 10, 8, 8, 1, 1, 1, 0),        # generic kernel
-                               Geometry(2, 6, 10, 64, 64, 3, 3, 1, 1)],     # persistent 3x3 kernel
+                               Geometry(2, 6, 16, 64, 64, 3, 3, 1, 1)],     # persistent 3x3 kernel
                          ids=["generic", "persistent3x3"])
 def test_z_rounding_is_nearest_even(g):
     """z = x0 + x1 with x0 = 1 + j*2^-7 and x1 in {2^-8, 3*2^-8, 2^-9}: exact fp32 sums that sit
