@@ -7,42 +7,15 @@ namespace {
 
 constexpr int NT = 256;
 
-// The BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per channel:
-// mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the difference
-// accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
-// eq_bias = beta - gamma*mean*inv_std, and the running update
-// next = (1 - momentum)*prev + momentum*batch (BatchNorm CUDA page, section 2.4).
-// Block b owns channels 4b..4b+3 and sums their columns of the R partial rows ([R][2][K],
-// sums then sums of squares).  rm_out/rv_out may alias rm_in/rv_in: each channel is
-// read before it is written, by the same thread.
-__global__ __launch_bounds__(NT) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
-                                                            const float *__restrict__ gamma,
-                                                            const float *__restrict__ beta, const float *rm_in,
-                                                            const float *rv_in, float eps, float momentum,
-                                                            float *__restrict__ scale, float *__restrict__ shift,
-                                                            float *__restrict__ saved_mean,
-                                                            float *__restrict__ saved_invstd, float *rm_out,
-                                                            float *rv_out)
+// The BN finalize (bn_finalize_channel) over the R partial rows ([R][2][K], sums then
+// sums of squares).  Block b owns channels 4b..4b+3.
+__global__ __launch_bounds__(NT) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K,
+                                                            BnFinalizeArgs f)
 {
     __shared__ double red[COLSUM_NT * 8];
     const int k0 = 4 * blockIdx.x;
     colsum_pair4(rows, R, K, k0, red);
-    if (threadIdx.x < 4) {
-        const int e = threadIdx.x, k = k0 + e;
-        const double mean = red[e] / M;
-        double var = red[4 + e] / M - mean * mean;
-        if (!(var > 0.0)) var = 0.0;
-        const double invstd = 1.0 / sqrt(var + (double)eps);
-        const double gm = (double)gamma[k];
-        scale[k] = (float)(gm * invstd);
-        shift[k] = (float)((double)beta[k] - gm * mean * invstd);
-        saved_mean[k] = (float)mean;
-        saved_invstd[k] = (float)invstd;
-        const double mo = (double)momentum;
-        const float rm = rm_in[k], rv = rv_in[k];
-        rm_out[k] = (float)((1.0 - mo) * (double)rm + mo * mean);
-        rv_out[k] = (float)((1.0 - mo) * (double)rv + mo * var);
-    }
+    if (threadIdx.x < 4) bn_finalize_channel(f, k0 + threadIdx.x, red[threadIdx.x], red[4 + threadIdx.x]);
 }
 
 // Normalise + ReLU + mask (CBR page, section 4.3): u = z*eq_scale + eq_bias, y = max(u, 0),
@@ -136,14 +109,10 @@ int train_partial_rows(const ConvGeom &g)
     return halo_eligible(g) ? halo_grid(g) : c3s2_eligible(g) ? c3s2_grid(g) : conv_plan(g).tiles_m;
 }
 
-hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, const float *gamma,
-                                 const float *beta, const float *rm_in, const float *rv_in, float eps,
-                                 float momentum, float *scale, float *shift, float *saved_mean,
-                                 float *saved_invstd, float *rm_out, float *rv_out, hipStream_t st, hipEvent_t e0,
-                                 hipEvent_t e1)
+hipError_t launch_stats_finalize(int rows, int K, const float *partials, const BnFinalizeArgs &fin, hipStream_t st,
+                                 hipEvent_t e0, hipEvent_t e1)
 {
-    return launch(stats_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, e0, e1, partials, rows, K, (double)M, gamma,
-                  beta, rm_in, rv_in, eps, momentum, scale, shift, saved_mean, saved_invstd, rm_out, rv_out);
+    return launch(stats_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, e0, e1, partials, rows, K, fin);
 }
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,

@@ -181,6 +181,8 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
     float *partials = (float *)ws_at(workspace, L.partials);
     float *scale = (float *)ws_at(workspace, L.scale);
     float *shift = (float *)ws_at(workspace, L.shift);
+    const BnFinalizeArgs fin{gamma, beta,  run_mean_in, run_var_in,   eps,          momentum,   (double)g.M,
+                             scale, shift, saved_mean,  saved_invstd, run_mean_out, run_var_out};
     // conv + channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
     const hipError_t ec =
         halo_eligible(g)   ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
@@ -189,9 +191,8 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
                            : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
                                                ev(events, 1));
     if (ec != hipSuccess) return CBR_E_HIP;
-    if (launch_stats_finalize(train_partial_rows(g), g.K, g.M, partials, gamma, beta, run_mean_in, run_var_in,
-                              eps, momentum, scale, shift, saved_mean, saved_invstd, run_mean_out, run_var_out, s,
-                              ev(events, 2), ev(events, 3)) != hipSuccess)
+    if (launch_stats_finalize(train_partial_rows(g), g.K, partials, fin, s, ev(events, 2), ev(events, 3)) !=
+        hipSuccess)
         return CBR_E_HIP;
     if (launch_bn_apply_relu_mask(g.M, g.K, z, scale, shift, y, (uint8_t *)relu_mask, s, ev(events, 4),
                                   ev(events, 5)) != hipSuccess)

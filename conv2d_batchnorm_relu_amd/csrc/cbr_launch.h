@@ -19,6 +19,15 @@ namespace cbr {
 
 enum ConvEpilogue { EPI_STATS = 0, EPI_BIAS_RELU = 1, EPI_PLAIN = 2 };
 
+// Arguments of the BN finalize: per-channel inputs and outputs (float [K] each).
+struct BnFinalizeArgs {
+    const float *gamma, *beta, *rm_in, *rv_in;
+    float eps, momentum;
+    double M;                     // samples per channel, N*P*Q
+    float *scale, *shift;         // eq_scale, eq_bias of the apply pass
+    float *saved_mean, *saved_invstd, *rm_out, *rv_out;
+};
+
 // Launches kernel k, recording e0 at its start and e1 at its end when either is set.
 template <typename Kern, typename... Args>
 inline hipError_t launch(Kern k, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, hipEvent_t e0,
@@ -77,10 +86,7 @@ hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, cons
                              const float *bias, uint16_t *out, float *partials, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-hipError_t launch_stats_finalize(int rows, int K, long M, const float *partials, const float *gamma,
-                                 const float *beta, const float *rm_in, const float *rv_in, float eps,
-                                 float momentum, float *scale, float *shift, float *saved_mean,
-                                 float *saved_invstd, float *rm_out, float *rv_out, hipStream_t st,
+hipError_t launch_stats_finalize(int rows, int K, const float *partials, const BnFinalizeArgs &fin, hipStream_t st,
                                  hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,

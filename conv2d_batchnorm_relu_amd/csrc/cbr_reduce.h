@@ -1,9 +1,9 @@
 // cbr_reduce.h -- per-channel column sums of a row-major [R][2K] float partials array
 // (row r: K sums, then K sums of a second quantity), accumulated in fp64 in a fixed
-// order, so results are reproducible bit for bit.
+// order, so results are reproducible bit for bit; and the BN finalize of one channel.
 #pragma once
 
-#include "cbr_common.h"
+#include "cbr_launch.h"
 
 namespace cbr {
 
@@ -52,6 +52,29 @@ __device__ inline void colsum_pair4(const float *__restrict__ rows, int R, int K
             for (int e = 0; e < 8; ++e) red[tid * 8 + e] += red[(tid + s) * 8 + e];
         __syncthreads();
     }
+}
+
+// The BN finalize of the CBR page, section 4.2 -- with N_ac = M samples per channel:
+// mean = sum/M, var = sumsq/M - mean^2 (clamped at 0; fp64 keeps the difference
+// accurate), inv_std = 1/sqrt(var + eps), eq_scale = gamma*inv_std,
+// eq_bias = beta - gamma*mean*inv_std, and the running update
+// next = (1 - momentum)*prev + momentum*batch (BatchNorm CUDA page, section 2.4).
+// rm_out/rv_out may alias rm_in/rv_in: channel k is read before it is written.
+__device__ inline void bn_finalize_channel(const BnFinalizeArgs &f, int k, double s1, double s2)
+{
+    const double mean = s1 / f.M;
+    double var = s2 / f.M - mean * mean;
+    if (!(var > 0.0)) var = 0.0;
+    const double invstd = 1.0 / sqrt(var + (double)f.eps);
+    const double gm = (double)f.gamma[k];
+    f.scale[k] = (float)(gm * invstd);
+    f.shift[k] = (float)((double)f.beta[k] - gm * mean * invstd);
+    f.saved_mean[k] = (float)mean;
+    f.saved_invstd[k] = (float)invstd;
+    const double mo = (double)f.momentum;
+    const float rm = f.rm_in[k], rv = f.rv_in[k];
+    f.rm_out[k] = (float)((1.0 - mo) * (double)rm + mo * mean);
+    f.rv_out[k] = (float)((1.0 - mo) * (double)rv + mo * var);
 }
 
 }  // namespace cbr
