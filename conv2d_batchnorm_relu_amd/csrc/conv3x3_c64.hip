@@ -3,28 +3,32 @@
 // per-channel sum and sum of squares of its output (the conv + genstats step of the CBR
 // page's training forward, section 4.1).
 //
-// One 512-thread workgroup per compute unit walks whole images in steps of TP = 4
-// output rows.  In LDS it keeps
-//   - the whole filter, 64 x 576 bf16, rows padded to 1168 bytes;
-//   - a ring of 10 input rows: the 6 rows a step reads (its output rows +-1) and the 4
-//     rows of the next step, which stream in while the step computes.  Row h (-1 <= h
-//     <= H) lives in slot (h + 1) % 10; the padding rows -1 and H are zero slots.  A slot
-//     holds W + 2 pixels of 64 channels (zero columns at both ends), 128 bytes each, whose
-//     eight 16-byte channel chunks are stored XOR-permuted by (pixel / 2) % 8, so that
-//     16 consecutive pixels of one fragment read hit 16 distinct 4-bank groups.
+// One 512-thread workgroup per compute unit (two waves per SIMD) walks whole images in
+// steps of TP = 4 output rows.
+//   - Wave w computes output channels 32j .. 32j + 31, j = w / 4, and keeps that half of
+//     the filter, 32 x 576 bf16, in registers (36 MFMA operand fragments, 144 VGPRs), so
+//     LDS only serves input pixels.  Waves w and w + 4 share a SIMD and the same pixel
+//     blocks: the SIMD holds both channel halves of its blocks.
+//   - LDS holds a ring of 10 input rows: the 6 rows a step reads (its output rows +-1)
+//     and the 4 rows of the next step, which stream in while the step computes.  Row h
+//     (-1 <= h <= H) lives in slot (h + 1) % 10; the padding rows -1 and H are zero slots.
+//     A slot holds W + 2 pixels of 64 channels (zero columns at both ends), 128 bytes
+//     each, whose eight 16-byte channel chunks are stored XOR-permuted by (pixel / 2) % 8,
+//     so that 16 consecutive pixels of one fragment read hit 16 distinct 4-bank groups.
+//   - Two staging buffers for a step's z (224 pixels x 128 bytes): the epilogues write
+//     one; during the next step every wave stores a share of it as whole 1 KB runs of
+//     pixel rows, which costs the memory pipeline a quarter of the cache-line
+//     operations of storing straight from the MFMA layout.
 // Input rows are copied from HBM straight into their slot with global-to-LDS loads (no
-// register staging, no separate ring write): a wave's load instruction moves 8 pixels,
-// and each lane fetches the channel chunk that the permutation puts in its 16 bytes.
-// Each input row is read from HBM once and serves all nine taps.
+// register staging): a wave's load instruction moves 8 pixels, and each lane fetches the
+// channel chunk that the permutation puts in its 16 bytes.  Each input row is read from
+// HBM once and serves all nine taps.  Row loads and z stores are issued from inside the
+// k-loops, one per k-step, rather than as a burst between steps.
 //
 // GEMM mapping: v_mfma_f32_32x32x16_bf16 with the filter as the A operand (32 output
 // channels) and the input pixels as the B operand (32 pixels), so each lane ends up
-// holding 4 consecutive output channels of one pixel (8-byte stores of z).  A step has
-// TP*W/32 pixel blocks (7 for W = 56) x 2 channel blocks.  Wave w owns channel block
-// w % 2 and a quarter of the pixel blocks; waves w and w ^ 4 share a SIMD and get
-// quarters (1, 0) or (3, 2), so every SIMD holds about half of one channel block.
-// A full step's z stores are issued during the next step's k-loop, so the z traffic
-// streams under the MFMAs instead of leaving as one burst per step.
+// holding 4 consecutive output channels of one pixel.  A step has TP*W/32 pixel blocks
+// (7 for W = 56); the waves on SIMD s take blocks s and s + 4.
 // The statistics are accumulated per lane in fp32 registers across the whole persistent
 // loop and reduced across lanes and waves once at the end: one partial per workgroup.
 #include <hip/hip_ext.h>
@@ -38,11 +42,15 @@ constexpr int HC = 64;                  // input channels
 constexpr int HK = 64;                  // output channels
 constexpr int TP = 4;                   // output rows per step
 constexpr int NSLOT = 10;               // ring slots: TP + 2 read, TP incoming
-constexpr int WROW = 9 * HC * 2 + 16;   // bytes per filter row (576 bf16 + 16 bytes of padding)
-constexpr int WBYTES = HK * WROW;       // 74,752
 constexpr int PXB = HC * 2;             // bytes per staged pixel
 constexpr int NT = 512;                 // threads: 8 waves, two per SIMD
+constexpr int NW = NT / 64;
+constexpr int NSIMD = 4;
 constexpr int MAXW = 56;
+constexpr int KSTEPS = 36;              // 9 taps x 4 chunks of 16 input channels
+constexpr int STG_BYTES = TP * MAXW * PXB;   // one step's z, pixel-major
+constexpr int STATS_BYTES = 16 * NT * 4;     // final cross-lane reduction area
+constexpr int FILTER_BYTES = HK * 72 * 16;    // the filter, staged once through LDS
 
 struct HaloParams {
     const uint16_t *x;
@@ -68,127 +76,145 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// Per pixel block: LDS byte address of staged pixel q + sx in the slot of tap row r
-// (xb[r][sx]), and the lane's chunk permutation of those pixels, pre-shifted and with
-// the lane's k-half folded in (cx[sx] = (hi ^ perm(q + sx)) << 4): the fragment of
-// 16-channel chunk kc is at xb[r][sx] + ((32 * kc) ^ cx[sx]).
+// Per pixel block: LDS address of the lane's staged pixel q in the slot of tap row r
+// (rb[r]), and the lane's chunk permutation of pixels q + sx, pre-shifted and with the
+// lane's k-half folded in (cx[sx] = (hi ^ perm(q + sx)) << 4): the fragment of tap
+// (r, sx), 16-channel chunk kc is at rb[r] + 128 sx + ((32 * kc) ^ cx[sx]).
 struct BlockAddr {
-    int xb[3][3];
+    int rb[3];
     int cx[3];
 };
 
-// Bf16 results of the previous full step, waiting to be stored: block bb, channel
-// group g at byte offset off[bb] + 16*g of buffer zr.
-struct Pending {
-    u32x2 data[2][4];
-    int off[2];
-    __amdgpu_buffer_rsrc_t zr;
+// LDS fragment reads in inline assembly, with explicit waits.  While global-to-LDS loads
+// are in flight the compiler waits for every outstanding LDS read before each use
+// (lgkmcnt(0)), which would drain the read-ahead below at every k-step; reads from
+// assembly are outside its tracking, and the k-loop waits for exactly the reads it
+// needs.  LDS reads complete in order, so "at most n outstanding" means all but the n
+// newest are done (other LDS or scalar memory operations only add to the count).
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr)
+{
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+
+// The fragment about to be used is tied to the wait, so that its use cannot be
+// scheduled above it.
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8 &x)
+{
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+
+// The 36 k-steps of one pixel block for the wave's 32 output channels: per k-step one
+// LDS fragment read and one MFMA, the filter fragment from registers.  Fragments are read
+// KD - 1 k-steps ahead.  side(integral_constant<T>) issues the memory instructions that
+// belong to k-step T.
+template <typename Side>
+struct KLoop {
+    static constexpr int KD = 3;
+    const bf16x8 (&wf)[KSTEPS];
+    const BlockAddr &ba;
+    f32x16 &acc;
+    Side &side;
+    bf16x8 xf[KD];
+
+    // Fragment read of k-step T (tap T / 4 = (r, sx), chunk T % 4) into set T % KD.
+    template <int T>
+    __device__ __forceinline__ void read()
+    {
+        constexpr int tap = T >> 2, kc = T & 3, r = tap / 3, sx = tap - 3 * r;
+        xf[T % KD] = lds_read16<128 * sx>(ba.rb[r] + ((32 * kc) ^ ba.cx[sx]));
+    }
+
+    template <int T>
+    __device__ __forceinline__ void step()
+    {
+        if constexpr (T + KD - 1 < KSTEPS) read<T + KD - 1>();
+        // the reads of k-steps T + 1 .. min(T + KD - 1, 35) may stay in flight
+        constexpr int newer = (KSTEPS - 1 - T) < (KD - 1) ? (KSTEPS - 1 - T) : (KD - 1);
+        lds_wait<newer>(xf[T % KD]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[T], xf[T % KD], T == 0 ? f32x16{} : acc, 0, 0, 0);
+        side(std::integral_constant<int, T>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (T + 1 < KSTEPS) step<T + 1>();
+    }
+
+    template <int T>
+    __device__ __forceinline__ void prefetch()
+    {
+        read<T>();
+        if constexpr (T + 1 < KD - 1) prefetch<T + 1>();
+    }
+
+    __device__ __forceinline__ void run()
+    {
+        prefetch<0>();
+        step<0>();
+    }
 };
 
-// The 36 k-steps of one step (9 taps x 4 chunks of 16 channels) for the pixel blocks in
-// MASK (bit bb: block b0 + bb).  A wave runs only one or two MFMAs per k-step, so its
-// fragments are read KD - 1 k-steps ahead (KD register sets) to cover the LDS latency.
-// With PM, the previous full step's results (blocks in PM) are stored in k-steps 2, 6,
-// ..., 30, so that they stream under the MFMAs.
-constexpr int KD = 2;
-
-template <uint32_t MASK, uint32_t PM>
-__device__ __forceinline__ void kloop(const uint8_t *lds, int wa, const BlockAddr (&ba)[2], f32x16 (&acc)[2],
-                                      const Pending &pend)
+// v_permlane16_swap exchanges the odd 16-lane rows of a with the even rows of b: after
+// it, lanes of even rows hold a of both pixels l and l + 16, lanes of odd rows b of
+// pixels l - 16 and l.  Lanes l and l ^ 16 hold the same channels, so a swap and an add
+// halve the registers a running per-channel sum needs.
+__device__ __forceinline__ void swap_rows(float &a, float &b)
 {
-    bf16x8 wf[KD], xf[KD][2];
-    auto rd = [&](int t, int b) {
-        const int tap = t >> 2, kc = t & 3, r = tap / 3, sx = tap - 3 * r;
-        wf[b] = *(const bf16x8 *)(lds + wa + tap * 128 + kc * 32);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// Statistics and staging of one pixel block.  The lane holds, for pixel l32 of the
+// block, channels 32j + 8g + 4hi + e in acc[4g + e] (32x32x16 layout: row
+// 8*(v/4) + 4*(l/32) + v%4).  Running sums s1[i], s2[i] (i = 4g + e, g < 2) of lane l
+// cover channel 32j + 8(g + 2 ((l / 16) % 2)) + 4hi + e over pixel pairs (l, l ^ 16);
+// with MASKED, lanes of pixels past the step (!use) add zeros.  The bf16 results go to
+// staging row px (16-byte chunk c of a row at position c ^ perm(px)).
+template <bool MASKED>
+__device__ __forceinline__ void epilogue(const f32x16 &acc, bool use, uint8_t *stg, int px, int j, int hi,
+                                         float (&s1)[8], float (&s2)[8])
+{
+    float v[16];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-            if (MASK & (1u << bb))
-                xf[b][bb] = *(const bf16x8 *)(lds + ba[bb].xb[r][sx] + ((32 * kc) ^ ba[bb].cx[sx]));
-    };
+    for (int c = 0; c < 16; ++c) v[c] = acc[c];
 #pragma unroll
-    for (int t = 0; t < KD - 1; ++t) rd(t, t);
+    for (int g = 0; g < 4; ++g)
+        *(u32x2 *)(stg + px * PXB + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
+            u32x2{pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int t = 0; t < 36; ++t) {
-        if (t + KD - 1 < 36) rd(t + KD - 1, (t + KD - 1) % KD);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < 16; ++c) v[c] = use ? v[c] : 0.f;
+    }
+    // squares first, then the swaps in place: no value is needed after its swap
+    float q[16];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-            if (MASK & (1u << bb))
-                acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t % KD], xf[t % KD][bb],
-                                                                  t == 0 ? f32x16{} : acc[bb], 0, 0, 0);
-        if constexpr (PM != 0) {
-            const int sidx = (t - 2) / 4;   // store slot of k-steps 2, 6, ..., 30
-            if (t >= 2 && (t - 2) % 4 == 0 && sidx < 8 && (PM & (1u << (sidx >> 2))))
-                __builtin_amdgcn_raw_buffer_store_b64(pend.data[sidx >> 2][sidx & 3], pend.zr,
-                                                      pend.off[sidx >> 2] + 16 * (sidx & 3), 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < 16; ++c) q[c] = v[c] * v[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        swap_rows(v[i], v[i + 8]);
+        s1[i] += v[i] + v[i + 8];
+        swap_rows(q[i], q[i + 8]);
+        s2[i] += q[i] + q[i + 8];
     }
 }
 
-// Full step: statistics of the blocks in MASK, and their results packed into pend.
-// The lane holds, for pixel l32 of each block, channels 32j + 8g + 4hi + e in
-// acc[bb][4g + e] (32x32x16 layout: row 8*(v/4) + 4*(l/32) + v%4).
-template <uint32_t MASK>
-__device__ __forceinline__ void finish(const f32x16 (&acc)[2], const int (&zoff)[2], __amdgpu_buffer_rsrc_t zr,
-                                       float (&s1)[4][4], float (&s2)[4][4], Pending &pend)
-{
-    pend.zr = zr;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        if (!(MASK & (1u << bb))) continue;
-        pend.off[bb] = zoff[bb];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float a0 = acc[bb][4 * g], a1 = acc[bb][4 * g + 1];
-            const float a2 = acc[bb][4 * g + 2], a3 = acc[bb][4 * g + 3];
-            pend.data[bb][g] = u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-            s1[g][0] += a0; s2[g][0] = fmaf(a0, a0, s2[g][0]);
-            s1[g][1] += a1; s2[g][1] = fmaf(a1, a1, s2[g][1]);
-            s1[g][2] += a2; s2[g][2] = fmaf(a2, a2, s2[g][2]);
-            s1[g][3] += a3; s2[g][3] = fmaf(a3, a3, s2[g][3]);
-        }
-    }
-}
-
-template <uint32_t PM>
-__device__ __forceinline__ void flush(const Pending &pend)
-{
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-        if (PM & (1u << bb))
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                __builtin_amdgcn_raw_buffer_store_b64(pend.data[bb][g], pend.zr, pend.off[bb] + 16 * g, 0, 0);
-}
-
-// Steps with missing pixels: statistics and immediate stores of the lanes in use.
-__device__ __forceinline__ void epilogue_masked(const f32x16 (&acc)[2], const int (&zoff)[2], const bool (&use)[2],
-                                                __amdgpu_buffer_rsrc_t zr, float (&s1)[4][4], float (&s2)[4][4])
-{
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        if (!use[bb]) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float a0 = acc[bb][4 * g], a1 = acc[bb][4 * g + 1];
-            const float a2 = acc[bb][4 * g + 2], a3 = acc[bb][4 * g + 3];
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)}, zr,
-                                                  zoff[bb] + 16 * g, 0, 0);
-            s1[g][0] += a0; s2[g][0] = fmaf(a0, a0, s2[g][0]);
-            s1[g][1] += a1; s2[g][1] = fmaf(a1, a1, s2[g][1]);
-            s1[g][2] += a2; s2[g][2] = fmaf(a2, a2, s2[g][2]);
-            s1[g][3] += a3; s2[g][3] = fmaf(a3, a3, s2[g][3]);
-        }
-    }
-}
+// A staged step awaiting its stores: d[k] holds run k of the half being stored (a run is
+// 1 KB, pixels 8q .. 8q + 7); nq runs in all, bound for zr.
+struct Staged {
+    u32x4 d[4];
+    int nq;                          // 0: nothing staged
+    __amdgpu_buffer_rsrc_t zr;
+};
 
 __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint8_t *wl = lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int simd = wave & (NSIMD - 1), j = wave >> 2;
     const int H = p.H, W = p.W, SLOT = p.slot_bytes;
     const uint32_t invW = p.invW;
     const int spi = (H + TP - 1) / TP;                        // steps per image
@@ -196,67 +222,115 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     const int hi = lane >> 5;                                 // k-half of the MFMA operands
     const int l32 = lane & 31;
     const int ipr = W / 8;                                    // 8-pixel load instructions per row
-    // Wave w runs on SIMD w % 4 beside wave w ^ 4.  Channel block j = w & 1; the pixel
-    // blocks are cut into quarters q0..q3 and SIMD pairs take (q1, q0) or (q3, q2).
-    const int j = wave & 1;
-    const int quarter = (wave < 4) ? ((wave & 2) ? 3 : 1) : ((wave & 2) ? 2 : 0);
+    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_u8 *)lds;
+    uint8_t *const stg0 = lds + NSLOT * SLOT;                 // two step staging buffers
 
-    // Stages input rows h0 .. h0 + nrows - 1 (each -1 <= h <= H + 3) of image n into their
-    // slots: image rows by global-to-LDS loads, the others as zeros.  Instruction gi
-    // (row ri, pixels 8i .. 8i+7) is issued by wave gi % 8; lane l moves pixel 8i + l/8,
-    // position l % 8, which holds channel chunk (l % 8) ^ perm(1 + 8i + l/8).
-    auto stage_rows = [&](int n, int h0, int nrows) {
-        for (int gi = wave; gi < nrows * ipr; gi += 8) {
-            const int ri = gi / ipr, i = gi - ri * ipr;
-            const int h = h0 + ri;
-            const int dst = WBYTES + ((h + 1) % NSLOT) * SLOT + (1 + 8 * i) * PXB;   // wave-uniform
-            if (h >= 0 && h < H) {
-                const int u = 1 + 8 * i + (lane >> 3);
-                const uint16_t *src =
-                    p.x + ((size_t)(n * H + h) * W + 8 * i + (lane >> 3)) * HC + (((lane & 7) ^ perm(u)) * 8);
-                __builtin_amdgcn_global_load_lds((const void *)src, (lds_u8 *)lds + dst, 16, 0, 0);
-            } else {
-                *(u32x4 *)(lds + dst + lane * 16) = u32x4{0, 0, 0, 0};
-            }
+    // Staging of input rows h0 .. h0 + nrows - 1 (each -1 <= h <= H + 3) of image n into
+    // their slots: image rows by global-to-LDS loads, the others as zeros.  Instruction
+    // gi (row ri = gi / ipr, pixels 8i .. 8i+7) is issued by wave gi % 8; lane l moves
+    // pixel 8i + l/8, position l % 8, which holds channel chunk (l % 8) ^ perm(1 + 8i + l/8).
+    auto stage_one = [&](int n, int h0, int gi, int ln) {
+        const int ri = gi / ipr, i = gi - ri * ipr;
+        const int h = h0 + ri;
+        const int dst = ((h + 1) % NSLOT) * SLOT + (1 + 8 * i) * PXB;   // wave-uniform
+        if (h >= 0 && h < H) {
+            const int u = 1 + 8 * i + (ln >> 3);
+            const uint16_t *src =
+                p.x + ((size_t)(n * H + h) * W + 8 * i + (ln >> 3)) * HC + (((ln & 7) ^ perm(u)) * 8);
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_u8 *)lds + dst, 16, 0, 0);
+        } else {
+            *(u32x4 *)(lds + dst + ln * 16) = u32x4{0, 0, 0, 0};
         }
     };
-
-    // Prologue: the filter into LDS (all of a thread's loads in flight first), the
-    // padding columns of every slot zeroed, the first image's rows -1..4 staged.
-    {
-        constexpr int WCH = HK * 72 / NT;   // 9 filter chunks of 16 bytes per thread
-        u32x4 wv[WCH];
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) wv[i] = ((const u32x4 *)p.w)[tid + NT * i];
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) {
-            const int c = tid + NT * i, row = c / 72, ch = c - row * 72;
-            *(u32x4 *)(wl + row * WROW + ch * 16) = wv[i];
+    auto stage_rows = [&](int n, int h0, int nrows) {
+        for (int gi = wave; gi < nrows * ipr; gi += NW) stage_one(n, h0, gi, lane);
+    };
+    // Load k (pixels 8k .. 8k + 7) of input row h of image n into its slot, for the
+    // row-per-memory-wave staging inside the k-loops (k < ipr).
+    auto stage_part = [&](int n, int h, int k, int ln) {
+        const int dst = ((h + 1) % NSLOT) * SLOT + (1 + 8 * k) * PXB;   // wave-uniform
+        if (h >= 0 && h < H) {
+            const int u = 1 + 8 * k + (ln >> 3);
+            const uint16_t *src =
+                p.x + ((size_t)(n * H + h) * W + 8 * k + (ln >> 3)) * HC + (((ln & 7) ^ perm(u)) * 8);
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_u8 *)lds + dst, 16, 0, 0);
+        } else {
+            *(u32x4 *)(lds + dst + ln * 16) = u32x4{0, 0, 0, 0};
         }
-    }
-    for (int c = tid; c < NSLOT * 16; c += NT) {
+    };
+    // The memory waves (j == 0: waves 0..3, which win the MFMA arbitration against
+    // their SIMD partner and so have time to spare) issue the row loads.  A step's 1 KB z
+    // runs q = wave % 4 + 4 (4 half + k), k < 4, go out in two halves of up to four: half
+    // 0 from the memory waves, half 1 from the others.  load_staged reads a half of
+    // staging buffer buf into sd.
+    auto load_staged = [&](Staged &sd, int buf, int half, int ln, bool wait_now = true) {
+        const uint8_t *sb = stg0 + buf * STG_BYTES;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int px = 8 * (simd + NSIMD * (4 * half + k)) + (ln >> 3);
+            const int pxc = px < TP * MAXW ? px : 0;   // runs past nq are not stored
+            sd.d[k] = *(const u32x4 *)(sb + pxc * PXB + (((ln & 7) ^ perm(pxc)) << 4));
+        }
+        // A use here makes the compiler wait for the reads now, not at the first store
+        // inside the k-loop, where its wait would also drain the k-loop's read-ahead.
+        if (wait_now) asm volatile("" ::"v"(sd.d[0]), "v"(sd.d[1]), "v"(sd.d[2]), "v"(sd.d[3]));
+    };
+    // Runs q >= nq lie past the end of zr (npix * 128 = nq * 1024 bytes): the buffer
+    // store drops them, so no condition is needed.
+    auto store_staged = [&](const Staged &sd, int half, int k, int ln) {
+        const int q = simd + NSIMD * (4 * half + k);
+        __builtin_amdgcn_raw_buffer_store_b128(sd.d[k], sd.zr, q * 1024 + ln * 16, 0, 0);
+    };
+
+    // The filter half into registers, through LDS: global-to-LDS loads put 16-byte chunk
+    // c of filter row r (KRSC: 72 chunks per output channel) at F + (64c + r) * 16, in the
+    // ring slots 6.. and the staging buffers, which the first k-loop does not touch yet.
+    // Load c gathers chunk c of all 64 rows (lane r), so the fragment reads below are
+    // conflict-free.  Fragment t of lane (l32, hi) is output channel 32j + l32, tap t / 4,
+    // input channels 16 (t % 4) + 8 hi .. + 7: chunk 8 (t / 4) + 2 (t % 4) + hi.  Meanwhile
+    // the first image's rows -1..4 stream into slots 0..5.
+    const int F = 6 * SLOT;
+    for (int c = wave; c < 72; c += NW)
+        __builtin_amdgcn_global_load_lds((const void *)(p.w + ((size_t)lane * 72 + c) * 8), (lds_u8 *)lds + F + c * 1024,
+                                         16, 0, 0);
+    for (int c = tid; c < 6 * 16; c += NT) {
         const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
-        *(u32x4 *)(lds + WBYTES + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
+        *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
     }
     if (nimg > 0) stage_rows(blockIdx.x, -1, TP + 2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // Per-lane running statistics: channel 32*j + 8*g + 4*hi + e.
-    float s1[4][4], s2[4][4];
+    bf16x8 wf[KSTEPS];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int t = 0; t < KSTEPS; ++t)
+        wf[t] = *(const bf16x8 *)(lds + F + (((t >> 2) * 8 + (t & 3) * 2 + hi) * 64 + 32 * j + l32) * 16);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // the filter area is free again
+    // The padding columns of slots 6..9 zeroed (the first k-loop's row loads fill the
+    // other columns).
+    for (int c = tid; c < 4 * 16; c += NT) {
+        const int slot = 6 + (c >> 4), col = (c & 8) ? W + 1 : 0;
+        *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
+    }
+
+    // Per-lane running statistics (layout: see epilogue).
+    float s1[8], s2[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s1[g][e] = 0.f;
-            s2[g][e] = 0.f;
-        }
+    for (int i = 0; i < 8; ++i) {
+        s1[i] = 0.f;
+        s2[i] = 0.f;
+    }
 
-    // Filter fragment base: row 32*j + l32, k-half hi (tap and chunk are immediates).
-    const int wa = (32 * j + l32) * WROW + hi * 16;
-
-    Pending pend;
-    uint32_t pm = 0;   // blocks of the previous full step still to be stored
+    Staged prev;          // the previous step, staged in buffer pbuf
+    prev.nq = 0;
+    prev.zr = make_rsrc(p.z, 0);   // nothing staged yet: every store is dropped
+    int pbuf = 1;
+    const bool memw = j == 0;                                 // a memory wave
+    constexpr int DMA_T0 = 4;                                 // k-step of the first row load
+    constexpr int DMA_MAX = MAXW / 8;                          // row loads per memory wave
+    static_assert(TP == NSIMD, "one staged row per memory wave");
+    static_assert(DMA_T0 + DMA_MAX <= KSTEPS, "the row loads fit in one k-loop");
+    static_assert(2 * 4 * NSIMD * 1024 >= STG_BYTES, "two halves of runs cover a step");
     for (int img = 0; img < nimg; ++img) {
         const int n = (int)blockIdx.x + img * (int)gridDim.x;
         if (img > 0) {
@@ -266,108 +340,125 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             __syncthreads();
         }
         for (int s = 0; s < spi; ++s) {
+            // Opaque per-step copy of the lane id: lane-derived addresses are recomputed
+            // each step instead of being hoisted into registers held through the k-loops.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int l32s = ln & 31, his = ln >> 5;
             const int p0 = s * TP;
             const int rows_s = min(TP, H - p0);
             const int npix = rows_s * W;
-            const int nblk = (npix + 31) >> 5;
-            const int b0 = (quarter * nblk) >> 2, b1 = ((quarter + 1) * nblk) >> 2;   // blocks [b0, b1), <= 2
-            const int nb = b1 - b0;
-            const bool full = npix == nblk * 32;
-
-            // The next step's rows p0 + 5 .. p0 + 8 stream into the 4 free slots.
-            if (s + 1 < spi) stage_rows(n, p0 + TP + 1, TP);
-            __builtin_amdgcn_sched_barrier(0);
-
-            const __amdgpu_buffer_rsrc_t zr = make_rsrc(p.z + ((size_t)n * H + p0) * W * HK, npix * HK * 2);
-            BlockAddr ba[2];
-            int zoff[2];
-            bool use[2];
+            const int nblk = (npix + 31) >> 5;   // <= 7 (W <= 56)
+            const int nb = (simd < nblk) + (simd + NSIMD < nblk);
+            const bool full = npix == 32 * nblk;   // every pixel block complete
+            // The next step's rows p0 + 5 .. p0 + 8 stream into the 4 free slots, memory
+            // wave w loading row p0 + 5 + w (after an image's last step these rows are past
+            // its end: the slots get zeros, which nothing reads before the next image
+            // restages them).  Rows narrower than 7 loads repeat their last load.
+            const int nload = TP * ipr;
+            const int h0n = p0 + TP + 1;
+            const int cbuf = pbuf ^ 1;
+            uint8_t *const stg = stg0 + cbuf * STG_BYTES;
+            // The previous step's z: the memory waves store the first half of its runs,
+            // the others the second half.
+            load_staged(prev, pbuf, j, ln);
+            if (nb == 0) {   // no k-loop to carry the memory traffic
+                for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
+                if (memw)
+                    for (int k = 0; k < ipr; ++k) stage_part(n, h0n + wave, k, ln);
+            }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int pi = 32 * (b0 + bb) + l32;
-                const bool valid = pi < npix;
-                const int pr = valid ? div_w(pi, invW) : 0;
-                const int q = valid ? pi - pr * W : 0;
-                use[bb] = valid && bb < nb;
-                zoff[bb] = 2 * (pi * HK + 32 * j + 4 * hi);
+                if (bb >= nb) break;
+                const int pi = 32 * (simd + NSIMD * bb) + l32s;
+                const bool use = pi < npix;
+                const int pr = use ? div_w(pi, invW) : 0;
+                const int q = use ? pi - pr * W : 0;
+                BlockAddr ba;
 #pragma unroll
                 for (int r = 0; r < 3; ++r) {
                     int sl = (p0 % NSLOT) + pr + r;        // slot of input row p0 + pr + r - 1
                     if (sl >= NSLOT) sl -= NSLOT;
                     if (sl >= NSLOT) sl -= NSLOT;
-#pragma unroll
-                    for (int sx = 0; sx < 3; ++sx) ba[bb].xb[r][sx] = WBYTES + sl * SLOT + (q + sx) * PXB;
+                    ba.rb[r] = (int)lbase + sl * SLOT + q * PXB;
                 }
 #pragma unroll
-                for (int sx = 0; sx < 3; ++sx) ba[bb].cx[sx] = (hi ^ perm(q + sx)) << 4;
-            }
+                for (int sx = 0; sx < 3; ++sx) ba.cx[sx] = (his ^ perm(q + sx)) << 4;
 
-            f32x16 acc[2];
-            if (full && nb == 2) {
-                if (pm == 3u)
-                    kloop<3u, 3u>(lds, wa, ba, acc, pend);
-                else if (pm == 1u)
-                    kloop<3u, 1u>(lds, wa, ba, acc, pend);
-                else
-                    kloop<3u, 0u>(lds, wa, ba, acc, pend);
-                finish<3u>(acc, zoff, zr, s1, s2, pend);
-                pm = 3u;
-            } else if (full && nb == 1) {
-                if (pm == 3u)
-                    kloop<1u, 3u>(lds, wa, ba, acc, pend);
-                else if (pm == 1u)
-                    kloop<1u, 1u>(lds, wa, ba, acc, pend);
-                else
-                    kloop<1u, 0u>(lds, wa, ba, acc, pend);
-                finish<1u>(acc, zoff, zr, s1, s2, pend);
-                pm = 1u;
-            } else {
-                if (pm == 3u) flush<3u>(pend);
-                if (pm == 1u) flush<1u>(pend);
-                pm = 0;
-                if (nb > 0) {
-                    kloop<3u, 0u>(lds, wa, ba, acc, pend);
-                    epilogue_masked(acc, zoff, use, zr, s1, s2);
+                f32x16 acc;
+                if (memw && bb == 0) {
+                    // k-steps 0..3: the first half of the previous step's z runs; 4..: the
+                    // row loads
+                    auto side = [&](auto tc) {
+                        constexpr int T = decltype(tc)::value;
+                        // an opaque lane id per k-step keeps each instruction's address
+                        // computation at its k-step instead of in registers held from the start
+                        int lt = ln;
+                        asm volatile("" : "+v"(lt));
+                        if constexpr (T < 4) {
+                            store_staged(prev, 0, T, lt);
+                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + DMA_MAX) {
+                            stage_part(n, h0n + wave, min(T - DMA_T0, ipr - 1), lt);
+                        }
+                    };
+                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
+                } else if (bb == 0) {
+                    // k-steps 0..3: the second half of the previous step's z runs
+                    auto side = [&](auto tc) {
+                        constexpr int T = decltype(tc)::value;
+                        if constexpr (T < 4) store_staged(prev, 1, T, ln);
+                    };
+                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
+                } else {
+                    auto side = [](auto) {};
+                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 }
+                if (full)
+                    epilogue<false>(acc, use, stg, pi, j, his, s1, s2);
+                else
+                    epilogue<true>(acc, use, stg, pi, j, his, s1, s2);
             }
 
             // The staged rows must have landed before any wave reads them: wait for this
             // wave's loads, then the barrier publishes every wave's.  The barrier also
-            // frees the slots this step read for the step after next.
+            // frees the slots this step read for the step after next, and publishes this
+            // step's staged z.
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            prev.nq = npix / 8;
+            prev.zr = make_rsrc(p.z + ((size_t)n * H + p0) * W * HK, npix * HK * 2);
+            pbuf = cbuf;
         }
     }
-    if (pm == 3u) flush<3u>(pend);
-    if (pm == 1u) flush<1u>(pend);
+    load_staged(prev, pbuf, j, lane);
+    for (int k = 0; k < 4; ++k) store_staged(prev, j, k, lane);
+    __syncthreads();   // every wave is done with the staging buffers and the ring
 
-    // Cross-lane sum through LDS, in the filter area (no longer read: the last step's
-    // barrier has passed; 64 KB <= WBYTES).  st[f][tid] holds entry f of the lane's
-    // flattened [s1 | s2]: entry 16*which + 4*g + e is channel 32j + 8g + 4hi + e.
-    float *st = (float *)wl;             // [32][NT]
+    // Cross-lane sum through LDS.  st[f][tid] holds entry f = 8*which + i of the lane's
+    // [s1 | s2].
+    float *st = (float *)lds;             // [16][NT]
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            st[(4 * g + e) * NT + tid] = s1[g][e];
-            st[(16 + 4 * g + e) * NT + tid] = s2[g][e];
-        }
+    for (int i = 0; i < 8; ++i) {
+        st[i * NT + tid] = s1[i];
+        st[(8 + i) * NT + tid] = s2[i];
+    }
     __syncthreads();
-    // Thread (f, jj, h) sums the 128 lanes of channel block jj with hi == h: waves
-    // jj, jj + 2, jj + 4, jj + 6 x 32 lanes, fixed order.
-    if (tid < 128) {
-        const int f = tid >> 2, jj = (tid >> 1) & 1, h = tid & 1;
-        const f32x4 *row = (const f32x4 *)(st + f * NT + 32 * h);
+    // Thread (which, k) sums channel k = 32j + 8g + 4h + e over the 4 waves of half j x
+    // the 16 lanes that hold it (hi == h, (l / 16) % 2 == g / 2; entry i = 4 (g % 2) + e),
+    // in a fixed order.
+    if (tid < 2 * HK) {
+        const int which = tid >> 6, k = tid & 63;
+        const int jk = k >> 5, g = (k >> 3) & 3, h = (k >> 2) & 1, e = k & 3;
+        const f32x4 *row =
+            (const f32x4 *)(st + (8 * which + 4 * (g & 1) + e) * NT + 256 * jk + 32 * h + 16 * (g >> 1));
         float a = 0.f;
 #pragma unroll
-        for (int w = jj; w < 8; w += 2)
+        for (int w = 0; w < NSIMD; ++w)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 const f32x4 q = row[16 * w + i];
                 a += (q[0] + q[1]) + (q[2] + q[3]);
             }
-        const int which = f >> 4, ge = f & 15;
-        const int k = 32 * jj + 8 * (ge >> 2) + 4 * h + (ge & 3);
         p.partials[(size_t)blockIdx.x * 2 * HK + which * HK + k] = a;
     }
 }
@@ -382,11 +473,18 @@ bool halo_eligible(const ConvGeom &g)
 
 int halo_grid(const ConvGeom &g) { return std::min(g.N, HALO_MAX_GRID); }
 
-size_t halo_lds_bytes(const ConvGeom &g) { return WBYTES + (size_t)NSLOT * (g.W + 2) * PXB; }
+size_t halo_lds_bytes(const ConvGeom &g)
+{
+    const size_t ring = (size_t)NSLOT * (g.W + 2) * PXB;
+    return std::max({ring + 2 * STG_BYTES, (size_t)6 * (g.W + 2) * PXB + FILTER_BYTES, (size_t)STATS_BYTES});
+}
 
 hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
                                     float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
+    static_assert(NSLOT * (MAXW + 2) * PXB + 2 * STG_BYTES <= HALO_MAX_LDS && STATS_BYTES <= HALO_MAX_LDS &&
+                      6 * (MAXW + 2) * PXB + FILTER_BYTES <= HALO_MAX_LDS,
+                  "LDS bound");
     HaloParams prm{x, w, z, partials, g.N, g.H, g.W, (g.W + 2) * PXB, (65536u + g.W - 1) / g.W};
     const size_t lds = halo_lds_bytes(g);
     static bool attr_set = false;
