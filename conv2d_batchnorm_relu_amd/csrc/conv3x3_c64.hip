@@ -276,10 +276,14 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
         if (wait_now) asm volatile("" ::"v"(sd.d[0]), "v"(sd.d[1]), "v"(sd.d[2]), "v"(sd.d[3]));
     };
     // Runs q >= nq lie past the end of zr (npix * 128 = nq * 1024 bytes): the buffer
-    // store drops them, so no condition is needed.
+    // store drops them, so no condition is needed.  The stores stream (nt) and write
+    // through to the device's coherence point (sc1): z is not read again in this kernel,
+    // and lines left dirty in L2 would have to be written back when the kernel ends,
+    // between it and the next kernel of the step.
+    constexpr int Z_POLICY = 2 | 16;   // nt | sc1
     auto store_staged = [&](const Staged &sd, int half, int k, int ln) {
         const int q = simd + NSIMD * (4 * half + k);
-        __builtin_amdgcn_raw_buffer_store_b128(sd.d[k], sd.zr, q * 1024 + ln * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(sd.d[k], sd.zr, q * 1024 + ln * 16, 0, Z_POLICY);
     };
 
     // The filter half into registers, through LDS: global-to-LDS loads put 16-byte chunk
@@ -355,7 +359,6 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             // wave w loading row p0 + 5 + w (after an image's last step these rows are past
             // its end: the slots get zeros, which nothing reads before the next image
             // restages them).  Rows narrower than 7 loads repeat their last load.
-            const int nload = TP * ipr;
             const int h0n = p0 + TP + 1;
             const int cbuf = pbuf ^ 1;
             uint8_t *const stg = stg0 + cbuf * STG_BYTES;
