@@ -330,7 +330,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     prev.zr = make_rsrc(p.z, 0);   // nothing staged yet: every store is dropped
     int pbuf = 1;
     const bool memw = j == 0;                                 // a memory wave
-    constexpr int DMA_T0 = 4;                                 // k-step of the first row load
+    constexpr int DMA_T0 = 6;                                 // k-step of the first row load
     constexpr int DMA_MAX = MAXW / 8;                          // row loads per memory wave
     static_assert(TP == NSIMD, "one staged row per memory wave");
     static_assert(DMA_T0 + DMA_MAX <= KSTEPS, "the row loads fit in one k-loop");
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             uint8_t *const stg = stg0 + cbuf * STG_BYTES;
             // The previous step's z: the memory waves store the first half of its runs,
             // the others the second half.
-            load_staged(prev, pbuf, j, ln);
+            load_staged(prev, pbuf, j, ln, false);   // waited for by the first store
             if (nb == 0) {   // no k-loop to carry the memory traffic
                 for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
                 if (memw)
@@ -390,26 +390,26 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
 
                 f32x16 acc;
                 if (memw && bb == 0) {
-                    // k-steps 0..3: the first half of the previous step's z runs; 4..: the
-                    // row loads
+                    // k-steps 2..5: the first half of the previous step's z runs (its LDS
+                    // reads have landed by then); 6..: the row loads
                     auto side = [&](auto tc) {
                         constexpr int T = decltype(tc)::value;
                         // an opaque lane id per k-step keeps each instruction's address
                         // computation at its k-step instead of in registers held from the start
                         int lt = ln;
                         asm volatile("" : "+v"(lt));
-                        if constexpr (T < 4) {
-                            store_staged(prev, 0, T, lt);
+                        if constexpr (T >= 2 && T < 6) {
+                            store_staged(prev, 0, T - 2, lt);
                         } else if constexpr (T >= DMA_T0 && T < DMA_T0 + DMA_MAX) {
                             stage_part(n, h0n + wave, min(T - DMA_T0, ipr - 1), lt);
                         }
                     };
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 } else if (bb == 0) {
-                    // k-steps 0..3: the second half of the previous step's z runs
+                    // k-steps 2..5: the second half of the previous step's z runs
                     auto side = [&](auto tc) {
                         constexpr int T = decltype(tc)::value;
-                        if constexpr (T < 4) store_staged(prev, 1, T, ln);
+                        if constexpr (T >= 2 && T < 6) store_staged(prev, 1, T - 2, ln);
                     };
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 } else {
