@@ -46,6 +46,10 @@ struct C3Params {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Chunk permutation of the z staging rows: 16-byte chunk c of pixel px sits at position
+// c ^ perm(px), so consecutive pixels' chunks spread over the LDS banks.
+__device__ __forceinline__ int perm(int px) { return (px >> 1) & 7; }
+
 // Widened filter [64][R][8][4] <- KRSC [64][R][S][3], zeros elsewhere.
 __global__ __launch_bounds__(NT) void widen_filter_c3_kernel(const uint16_t *__restrict__ w, int R, int S,
                                                              uint16_t *__restrict__ wexp)
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
     const int j = wave >> 1, blk0 = UPW * (wave & 1);
     const int hi = lane >> 5, l32 = lane & 31;
     const int wa = (32 * j + l32) * p.WRB + hi * 16;
-    int xa[UPW], zoff[UPW];
+    int xa[UPW];
     bool valid[UPW];
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
@@ -118,7 +122,6 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
         const int pr = pi / Q, q = pi - pr * Q;
         valid[u] = pr < TP && p0 + pr < p.P;
         xa[u] = valid[u] ? KOUT * p.WRB + 2 * pr * p.RB + 2 * q * 8 + hi * 16 : KOUT * p.WRB;
-        zoff[u] = valid[u] ? 2 * ((((n * p.P + p0 + pr) * Q + q) * KOUT) + 32 * j + 4 * hi) : 0;
     }
 
     // k-step t: tap row r = t/2, taps s = 4*(t%2) .. +3 (lane half hi: two of them).
@@ -152,7 +155,11 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
     }
 
     // Epilogue: lane holds, for pixel l32 of each block, channels 32j + 8g + 4hi + e in
-    // acc[u][4g + e]; bf16 stores of z and per-lane statistics.
+    // acc[u][4g + e].  Per-lane statistics; z goes through LDS (the staged rows and the
+    // filter are free once every wave is past the barrier) into pixel-major order, 16-byte
+    // chunk c of band pixel px at (c ^ perm(px)) << 4, and leaves as 1 KB runs of whole
+    // 128-byte pixel rows: storing straight from the MFMA layout touches 32 cache lines per
+    // instruction with 16 bytes each, which the memory pipeline processes line by line.
     float s1[4][4], s2[4][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -161,14 +168,16 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
             s1[g][e] = 0.f;
             s2[g][e] = 0.f;
         }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
         if (!valid[u]) continue;
+        const int px = 32 * (blk0 + u) + l32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const float a0 = acc[u][4 * g], a1 = acc[u][4 * g + 1];
             const float a2 = acc[u][4 * g + 2], a3 = acc[u][4 * g + 3];
-            *(u32x2 *)((uint8_t *)p.z + (size_t)(uint32_t)zoff[u] + 16 * g) =
+            *(u32x2 *)(lds + px * 128 + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
                 u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
             s1[g][0] += a0; s2[g][0] = fmaf(a0, a0, s2[g][0]);
             s1[g][1] += a1; s2[g][1] = fmaf(a1, a1, s2[g][1]);
@@ -176,9 +185,24 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
             s1[g][3] += a3; s2[g][3] = fmaf(a3, a3, s2[g][3]);
         }
     }
+    __syncthreads();
+    {
+        // The band's rows are contiguous in z (NHWC): npx pixels from pixel (n, p0, 0).
+        const int npx = min(TP, p.P - p0) * Q;
+        const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+            p.z + ((size_t)n * p.P + p0) * Q * KOUT, 0, npx * KOUT * 2, 0x00020000);
+        // sc1 without nt: measured, the z lines then still sit in the last-level cache for
+        // the normalisation pass that reads them next, and the stores run as fast.
+        constexpr int Z_POLICY = 16;
+        for (int q = wave; q < (npx + 7) / 8; q += NT / 64) {
+            const int px = 8 * q + (lane >> 3);   // runs past npx: the buffer drops the store
+            const u32x4 v = *(const u32x4 *)(lds + px * 128 + (((lane & 7) ^ perm(px)) << 4));
+            __builtin_amdgcn_raw_buffer_store_b128(v, zr, q * 1024 + lane * 16, 0, Z_POLICY);
+        }
+    }
 
-    // Cross-lane sum through LDS (the staged rows are no longer read once every wave is
-    // past the barrier): st[f][tid], f = 16*which + 4*g + e for channel 32j + 8g + 4hi + e.
+    // Cross-lane sum through LDS, once every wave has read its z runs:
+    // st[f][tid], f = 16*which + 4*g + e for channel 32j + 8g + 4hi + e.
     __syncthreads();
     float *st = (float *)lds;   // 32 x NT floats = 32 KB
 #pragma unroll
@@ -229,7 +253,8 @@ size_t c3s2_lds_bytes(const ConvGeom &g)
 {
     const int NR = 2 * (TP - 1) + g.R;
     const size_t stage = (size_t)KOUT * (g.R * 64 + 16) + (size_t)NR * c3_lw(g) * 8;
-    return std::max(stage, (size_t)32 * NT * 4);
+    const size_t zstage = (size_t)32 * NBLK * KOUT * 2;   // every pixel block of a band
+    return std::max({stage, zstage, (size_t)32 * NT * 4});
 }
 
 size_t c3s2_wexp_bytes(const ConvGeom &g) { return (size_t)KOUT * g.R * 32 * 2; }
