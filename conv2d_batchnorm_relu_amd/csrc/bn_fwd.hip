@@ -106,7 +106,10 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
 
 int train_partial_rows(const ConvGeom &g)
 {
-    return halo_eligible(g) ? halo_grid(g) : c3s2_eligible(g) ? c3s2_grid(g) : conv_plan(g).tiles_m;
+    return halo_eligible(g)                ? halo_grid(g)
+           : c3s2_eligible(g)              ? c3s2_grid(g)
+           : igemm_eligible(g, EPI_STATS) ? igemm_partial_rows(g)
+                                           : conv_plan(g).tiles_m;
 }
 
 hipError_t launch_stats_finalize(int rows, int K, const float *partials, const BnFinalizeArgs &fin, hipStream_t st,

@@ -82,6 +82,14 @@ struct WgradPlan {
 };
 WgradPlan wgrad_plan(int M, int K, int Kg);
 
+// Persistent large-tile implicit-GEMM conv (C % 32 == 0, K a multiple of 128): at most
+// 256 workgroups, each over a contiguous range of output pixels; with EPI_STATS one
+// partial row per workgroup.  launch_conv_fprop takes it whenever it is eligible.
+bool igemm_eligible(const ConvGeom &g, int epi);
+int igemm_partial_rows(const ConvGeom &g);
+hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w, const float *bias,
+                             uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+
 hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w,
                              const float *bias, uint16_t *out, float *partials, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

@@ -345,6 +345,7 @@ hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, cons
                              const float *bias, uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0,
                              hipEvent_t e1)
 {
+    if (igemm_eligible(g, epi)) return launch_conv_igemm(g, epi, x, w, bias, out, partials, st, e0, e1);
     const ConvPlan p = conv_plan(g);
     ConvParams prm{g, x, w, bias, out, partials};
     dim3 grid(p.tiles_m, p.tiles_n);

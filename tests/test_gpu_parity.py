@@ -88,6 +88,45 @@ def test_train_forward_first_layer(g):
     H.check_train(g, d, res, ora)
 
 
+# The persistent large-tile conv (C % 32 == 0, K a multiple of 128; at most 256
+# workgroups over contiguous pixel ranges).  K = 256 with at most 224 pixels per
+# workgroup runs one 224 x 256 chunk per workgroup (training forward, inference, data
+# gradient); the 256 x 128 multi-chunk form (several chunks per workgroup, a short last
+# chunk, several channel chunks) is switched off, and those shapes run the generic conv.
+# Also 1x1 / 5x5 / stride 2 and C = 96.
+IGEMM_TRAIN_GEOMS = [
+    Geometry(3, 13, 11, 64, 256, 3, 3, 1, 1),      # ragged ranges: 31 pixels per workgroup
+    Geometry(256, 10, 20, 32, 256, 1, 1, 1, 0),    # 200 pixels per workgroup, one slice
+    Geometry(16, 14, 14, 96, 256, 3, 3, 2, 1),     # stride 2, three slices per tap
+]
+IGEMM_INFER_GEOMS = IGEMM_TRAIN_GEOMS + [
+    Geometry(3, 160, 160, 32, 128, 3, 3, 1, 1),    # 300 pixels per workgroup: chunks of 256 and 44
+    Geometry(2, 200, 160, 32, 256, 1, 1, 1, 0),    # 250 per workgroup: 256 x 128 chunks, two channel chunks
+    Geometry(2, 99, 101, 64, 128, 3, 3, 2, 1),     # stride 2, padding on every side
+    Geometry(2, 19, 23, 32, 128, 5, 5, 1, 2),      # 5x5
+    Geometry(4, 14, 14, 64, 384, 1, 1, 1, 0),      # three channel chunks
+]
+
+
+@pytest.mark.parametrize("g", IGEMM_TRAIN_GEOMS, ids=str)
+def test_train_forward_large_tile(g):
+    H.log(f"train fwd (large-tile conv) {g}")
+    d = draw(g, "train", 17)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
+@pytest.mark.parametrize("g", IGEMM_INFER_GEOMS, ids=str)
+def test_infer_large_tile(g):
+    H.log(f"infer (large-tile conv) {g}")
+    d = draw(g, "infer", 18)
+    y = H.gpu_infer(g, d)
+    ref = H.oracle.forward_infer(H.oshape(g), d["x"], d["w"], d["bias"], d["gamma"], d["beta"],
+                                 d["run_mean"], d["run_var"], 1e-5)
+    H.assert_close(y, ref, "infer y")
+
+
 @pytest.mark.parametrize("g", INFER_GEOMS, ids=str)
 def test_infer_small(g):
     H.log(f"infer {g}")
@@ -116,6 +155,8 @@ BWD_GEOMS = [
     (Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1), False),  # stride 2: first-layer form, no dx
     (Geometry(2, 31, 29, 3, 64, 7, 7, 2, 3), False),   # Cin=3 7x7 s2 weight gradient
     (Geometry(4, 14, 14, 64, 72, 1, 1, 1, 0), True),
+    (Geometry(2, 12, 12, 128, 128, 3, 3, 1, 1), True),   # data gradient on 256 x 128 chunks
+    (Geometry(3, 13, 11, 256, 64, 3, 3, 1, 1), True),    # data gradient: 64 -> 256 channels
 ]
 
 
