@@ -11,9 +11,10 @@
 //     (v_mfma_f32_32x32x16_bf16, the filter as the A operand, so a lane's results are
 //     four consecutive channels of one pixel).  Large wave tiles keep the LDS fragment
 //     reads per MFMA low.
-//   * Reduction slices of BK = 32 (inside one filter tap, since C % 32 == 0) move from
-//     global memory straight into LDS (global-to-LDS loads, 64-byte rows, 16-byte chunks
-//     XOR-permuted by row so fragment reads are conflict-free), NSTAGE slices in flight.
+//   * Reduction slices of BK = 64 (C % 64 == 0) or 32 elements, inside one filter tap,
+//     move from global memory straight into LDS (buffer-to-LDS loads, 128- or 64-byte
+//     rows, 16-byte chunks XOR-permuted by row so fragment reads are conflict-free),
+//     NSTAGE slices in flight.
 //     Padding taps and pixels past the range get out-of-range buffer offsets (zeros).  The slice
 //     sequence runs on across chunk boundaries, so a chunk's epilogue overlaps the next
 //     chunk's first loads.
@@ -29,8 +30,6 @@
 namespace cbr {
 namespace {
 
-constexpr int BK = 32;      // reduction elements per slice
-constexpr int RB = 2 * BK;  // bytes per staged row
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -44,7 +43,7 @@ struct IgParams {
     int N, H, W, C, K, R, S;
     int sh, sw, ph, pw;
     int P, Q, M, Kg;
-    int ksteps;        // Kg / BK
+    int ksteps;        // Kg / BK slices per chunk
     int rows_per_wg;   // contiguous output pixels per workgroup
     int ntn;           // K / BN
 };
@@ -94,18 +93,16 @@ __device__ __forceinline__ void read_frag_row(bf16x8 (&f)[N], uint32_t base)
     }
 }
 
-// The MFMAs of one fragment set: acc[i][j] += A(filter j) * B(pixels i).  Unless ALL,
-// pixel blocks at or past nbv hold no pixel and are skipped.
-template <int MI, int NJ, bool ALL>
-__device__ __forceinline__ void mfma_set(f32x16 (&acc)[MI][NJ], const bf16x8 (&a)[NJ], const bf16x8 (&b)[MI], int nbv)
+// The MFMAs of one fragment set on the first NB pixel blocks: acc[i][j] += A(filter j) *
+// B(pixels i).  NB is a template argument so the MFMA sequence has no branches: a branch
+// per block makes the compiler move the accumulators between register files each time.
+template <int MI, int NJ, int NB>
+__device__ __forceinline__ void mfma_set(f32x16 (&acc)[MI][NJ], const bf16x8 (&a)[NJ], const bf16x8 (&b)[MI])
 {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        if (ALL || i < nbv) {
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[i], acc[i][j], 0, 0, 0);
-        }
-    }
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[i], acc[i][j], 0, 0, 0);
 }
 
 // Ties a register to the preceding wait, so its use cannot be scheduled above it.
@@ -135,21 +132,26 @@ __device__ __forceinline__ void vm_wait_steps(int n)
 // MI, NJ: pixel / channel blocks of 32 per wave; WGM x (4 / WGM) waves per workgroup.
 // ALIAS: every workgroup has at most one chunk, so the epilogue may reuse the slice
 // buffers; otherwise the staging tile has its own LDS.
-template <int MI, int NJ, int WGM, int WGN, int NSTAGE, int EPI, bool ALIAS>
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI, bool ALIAS>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams p)
 {
     constexpr int NW = WGM * WGN, NT = 64 * NW;
     constexpr int BM = 32 * MI * WGM, BN = 32 * NJ * WGN;
+    constexpr int RB = 2 * BK;                    // bytes per staged row
+    constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+    constexpr int RPI = 1024 / RB;                // rows per 1 KB load instruction
+    constexpr int KH = BK / 16;                   // MFMA k-steps per slice
     constexpr int ROWS = BM + BN;                 // staged rows per slice
-    constexpr int NINS = ROWS / 16;               // 1 KB load instructions per slice
+    constexpr int NINS = ROWS / RPI;              // load instructions per slice
     constexpr int IPW = (NINS + NW - 1) / NW;     // per wave, at most
     constexpr int LMIN = NINS / NW;               // per wave, at least
     constexpr int STAGE_B = ROWS * RB;
     constexpr int STG_ROW = 2 * BN;               // staging bytes per pixel
     constexpr int STG_OFF = ALIAS ? 0 : NSTAGE * STAGE_B;
     constexpr int NF = NJ * 32;                   // statistics values per lane
-    static_assert(BN >= 128 && BM % 32 == 0, "tile shape");
-    static_assert(!ALIAS || (NSTAGE * STAGE_B >= BM * STG_ROW && NSTAGE * STAGE_B >= NW * 64 * NF * 4),
+    constexpr int SCR_B = EPI == EPI_STATS ? NW * 64 * NF * 4 : 0;   // statistics scratch
+    static_assert(BN >= 128 && BM % 32 == 0 && (BK == 32 || BK == 64), "tile shape");
+    static_assert(!ALIAS || (NSTAGE * STAGE_B >= BM * STG_ROW && NSTAGE * STAGE_B >= SCR_B),
                   "the epilogue must fit the slice buffers");
 
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int l32 = lane & 31, hi = lane >> 5;
     const int wm = wave / WGN, wn = wave % WGN;
-    float *stat_acc = (float *)(lds + (ALIAS ? NSTAGE * STAGE_B : NSTAGE * STAGE_B + std::max(BM * STG_ROW, NW * 64 * NF * 4)));
+    float *stat_acc = (float *)(lds + (ALIAS ? NSTAGE * STAGE_B : NSTAGE * STAGE_B + std::max(BM * STG_ROW, SCR_B)));
 
     const int r0 = blockIdx.x * p.rows_per_wg;
     const int r1 = min(p.M, r0 + p.rows_per_wg);
@@ -170,15 +172,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         for (int i = tid; i < 2 * p.K; i += NT) stat_acc[i] = 0.f;
     }
 
-    // ---- slice loads: instruction u (rows 16u .. 16u + 15) is issued by wave u % NW ----
-    // Lane l moves staged row 16u + l/4, position l % 4, which holds the row's 16-byte
-    // chunk (l % 4) ^ perm, perm = (row / 4) % 4 = (l / 16) % 4.
+    // ---- slice loads: instruction u (rows RPI*u .. RPI*u + RPI - 1) is issued by wave
+    // u % NW.  Lane l moves staged row RPI*u + l / CPR, position l % CPR, which holds the
+    // row's 16-byte chunk (l % CPR) ^ perm(row), perm(row) = (row / (256 / RB)) % CPR: the
+    // 16 rows a fragment read covers then spread over all 64 LDS banks.
     // Buffer resources: a padding tap or a pixel past the range gets an offset past the
     // end, and the load writes zeros to LDS.
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, 2 * p.N * p.H * p.W * p.C, 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, 0, 2 * p.K * p.Kg, 0x00020000);
-    const int gc16 = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+    auto perm = [](int row) __attribute__((always_inline)) { return (row / (256 / RB)) % CPR; };
     // Per instruction: d_off = byte offset of the lane's row (pixel rows: of input pixel
     // (n, p*sh - ph, q*sw - pw), channel 0), plus its chunk; d_msk (pixel rows) = bit r of
     // the filter rows and bit 16 + s of the filter columns whose taps fall inside the
@@ -186,14 +189,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     int d_off[IPW], d_msk[IPW];
     int dchunk = -1, dks = 0, dr = 0, ds = 0, dc0 = 0;
     const int PQ = p.P * p.Q;
-    auto dma_chunk = [&](int c) {   // per-lane row data of chunk c
+    auto dma_chunk = [&](int c) __attribute__((always_inline)) {   // per-lane row data of chunk c
         const int mc = c / p.ntn, n0 = (c - mc * p.ntn) * BN;
         const int cm0 = r0 + mc * BM;
 #pragma unroll
         for (int t = 0; t < IPW; ++t) {
             const int u = wave + NW * t;
-            const int sr = 16 * u + (lane >> 2);
-            if (u < BM / 16) {
+            const int sr = RPI * u + lane / CPR;
+            const int gc16 = ((lane % CPR) ^ perm(sr)) * 16;
+            if (u < BM / RPI) {
                 const int m = cm0 + sr;
                 int msk = 0, off = 0;
                 if (m < r1) {
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
             }
         }
     };
-    auto dma_issue = [&](int g) {   // slice g (issued in order g = 0, 1, 2, ...)
+    auto dma_issue = [&](int g) __attribute__((always_inline)) {   // slice g (issued in order g = 0, 1, 2, ...)
         if (dks == 0) {
             ++dchunk;
             dma_chunk(dchunk);
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         for (int t = 0; t < IPW; ++t) {
             const int u = wave + NW * t;
             if (u >= NINS) break;
-            if (u < BM / 16) {
+            if (u < BM / RPI) {
                 const bool ok = (d_msk[t] & tapbits) == tapbits;
                 buffer_load_lds16(xr, (lds_u8 *)lds + dst + u * 1024, ok ? d_off[t] + toff : (int)OOB);
             } else {
@@ -247,24 +251,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
 
     // ---- fragments ----
     // Filter fragment j: staged row BM + wn*32*NJ + 32j + l32; pixel fragment i: staged
-    // row wm*32*MI + 32i + l32; both read chunk 2kh + hi at position (2kh + hi) ^ pa.
-    const int pa = (l32 >> 2) & 3;
-    uint32_t fa[2], xa[2];
+    // row wm*32*MI + 32i + l32; both read chunk 2kh + hi at position (2kh + hi) ^ pa
+    // (the row bases are multiples of 32, so perm(row) = perm(l32)).
+    const int pa = perm(l32);
+    uint32_t fa[KH], xa[KH];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < KH; ++kh) {
         const int pos = ((2 * kh + hi) ^ pa) << 4;
         fa[kh] = lbase + (BM + wn * 32 * NJ + l32) * RB + pos;
         xa[kh] = lbase + (wm * 32 * MI + l32) * RB + pos;
     }
     bf16x8 af[2][NJ], bf[2][MI];
-    auto read_frags = [&](bf16x8 (&a)[NJ], bf16x8 (&b)[MI], int g, int kh) {
+    auto read_frags = [&](bf16x8 (&a)[NJ], bf16x8 (&b)[MI], int g, int kh) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)((g % NSTAGE) * STAGE_B);
         read_frag_row<0, NJ, 32 * RB>(a, fa[kh] + so);
         read_frag_row<0, MI, 32 * RB>(b, xa[kh] + so);
     };
 
     f32x16 acc[MI][NJ];
-    auto zero_acc = [&]() {
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     };
 
     // ---- epilogue of chunk c ----
-    auto epilogue = [&](int c) {
+    auto epilogue = [&](int c) __attribute__((always_inline)) {
         const int mc = c / p.ntn, n0 = (c - mc * p.ntn) * BN;
         const int cm0 = r0 + mc * BM;
         const int nvalid = min(BM, r1 - cm0);
@@ -389,46 +394,66 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         read_frags(af[0], bf[0], 0, 0);
     }
     zero_acc();
-    int cks = 0, cchunk = 0;
-    int nbv = MI;   // pixel blocks of this wave that hold a pixel, current chunk
-    {
-        const int nv = min(BM, r1 - r0) - wm * 32 * MI;
-        nbv = nv <= 0 ? 0 : min(MI, (nv + 31) / 32);
-    }
-    for (int g = 0; g < total; ++g) {
-        if (g + NSTAGE - 1 < total) dma_issue(g + NSTAGE - 1);
-        read_frags(af[1], bf[1], g, 1);
-        lgkm_wait<MI + NJ>();
+    // One chunk's slices g0 .. g0 + ksteps - 1 with NB pixel blocks per wave; the MFMA
+    // count is fixed for the whole chunk (the switch below picks the instance), so the
+    // accumulators stay in place through the loop.
+    auto chunk_loop = [&](auto nbc, int g0) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nbc)::value;
+        for (int ks = 0; ks < p.ksteps; ++ks) {
+            const int g = g0 + ks;
+            // k-steps 0 .. KH-2: read the next k-step's fragments, then the MFMAs of this one;
+            // the next slice's loads go out behind the first MFMAs, which run meanwhile
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) after_wait(af[0][j]);
+            for (int kh = 0; kh + 1 < KH; ++kh) {
+                bf16x8 (&an)[NJ] = af[(kh + 1) & 1];
+                bf16x8 (&bn)[MI] = bf[(kh + 1) & 1];
+                read_frags(an, bn, g, kh + 1);
+                lgkm_wait<MI + NJ>();
 #pragma unroll
-        for (int i = 0; i < MI; ++i) after_wait(bf[0][i]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_set<MI, NJ, ALIAS>(acc, af[0], bf[0], nbv);
-        __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait<0>();
+                for (int j = 0; j < NJ; ++j) after_wait(af[kh & 1][j]);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) after_wait(af[1][j]);
+                for (int i = 0; i < MI; ++i) after_wait(bf[kh & 1][i]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_set<MI, NJ, NB>(acc, af[kh & 1], bf[kh & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kh == 0 && g + NSTAGE - 1 < total) dma_issue(g + NSTAGE - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // last k-step: its fragments in, the next slice landed, every wave past this
+            // slice's buffer; then the next slice's first fragments under its MFMAs
+            lgkm_wait<0>();
 #pragma unroll
-        for (int i = 0; i < MI; ++i) after_wait(bf[1][i]);
-        const bool more = g + 1 < total;
-        if (more) vm_wait_steps<LMIN>(min(NSTAGE - 2, total - 2 - g));
-        barrier();
-        const bool chunk_end = ++cks == p.ksteps;
-        if (more && !chunk_end) read_frags(af[0], bf[0], g + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_set<MI, NJ, ALIAS>(acc, af[1], bf[1], nbv);
-        __builtin_amdgcn_sched_barrier(0);
-        if (chunk_end) {
-            epilogue(cchunk);
-            zero_acc();
-            cks = 0;
-            ++cchunk;
-            const int mc = cchunk / p.ntn;
-            const int nv = min(BM, r1 - (r0 + mc * BM)) - wm * 32 * MI;
-            nbv = nv <= 0 ? 0 : min(MI, (nv + 31) / 32);
-            if (more) read_frags(af[0], bf[0], g + 1, 0);
+            for (int j = 0; j < NJ; ++j) after_wait(af[(KH - 1) & 1][j]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) after_wait(bf[(KH - 1) & 1][i]);
+            if (g + 1 < total) vm_wait_steps<LMIN>(min(NSTAGE - 2, total - 2 - g));
+            barrier();
+            if (ks + 1 < p.ksteps) read_frags(af[0], bf[0], g + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_set<MI, NJ, NB>(acc, af[(KH - 1) & 1], bf[(KH - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    for (int c = 0; c < nchunk; ++c) {
+        const int g0 = c * p.ksteps;
+        if constexpr (ALIAS) {
+            // single-chunk workgroups compute every block (a chunk of at most BM pixels;
+            // a partial block costs as much as a full one)
+            chunk_loop(std::integral_constant<int, MI>{}, g0);
+        } else {
+            const int mc = c / p.ntn;
+            const int nv = min(BM, r1 - (r0 + mc * BM)) - wm * 32 * MI;   // this wave's pixels
+            const int nbv = nv <= 0 ? 0 : min(MI, (nv + 31) / 32);
+            static_assert(MI <= 4, "block-count instances below");
+            if (nbv >= MI) chunk_loop(std::integral_constant<int, MI>{}, g0);
+            else if (nbv == 3) { if constexpr (MI > 3) chunk_loop(std::integral_constant<int, 3>{}, g0); }
+            else if (nbv == 2) { if constexpr (MI > 2) chunk_loop(std::integral_constant<int, 2>{}, g0); }
+            else if (nbv == 1) { if constexpr (MI > 1) chunk_loop(std::integral_constant<int, 1>{}, g0); }
+            else chunk_loop(std::integral_constant<int, 0>{}, g0);
+        }
+        epilogue(c);
+        zero_acc();
+        if (g0 + p.ksteps < total) read_frags(af[0], bf[0], g0 + p.ksteps, 0);
     }
 
     if constexpr (EPI == EPI_STATS) {
@@ -438,8 +463,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     }
 }
 
+// Multi-chunk form: MI x NJ blocks per wave, WGM x WGN waves (256 x 128 chunks).
+#define IG_A_MI 4
+#define IG_A_NJ 2
+#define IG_A_WGM 2
+#define IG_A_WGN 2
+
 struct IgConfig {
-    int mi, nj, wgm, wgn, nstage;
+    int mi, nj, wgm, wgn, bk, nstage;
     bool alias;
     int bm() const { return 32 * mi * wgm; }
     int bn() const { return 32 * nj * wgn; }
@@ -451,41 +482,45 @@ int ig_rows_per_wg(const ConvGeom &g) { return (g.M + ig_grid(g) - 1) / ig_grid(
 
 // K = 256 with at most 224 pixels per workgroup: one 224 x 256 chunk per workgroup, eight
 // waves side by side over the channels (two per SIMD); otherwise 256 x 128 chunks, four
-// waves in a 2 x 2 grid.
+// waves in a 2 x 2 grid.  Slices of 64 reduction elements (whole 128-byte rows) when
+// C % 64 == 0, two in flight; else of 32, four in flight.
 IgConfig ig_config(const ConvGeom &g)
 {
-    if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, 4, true};
-    return IgConfig{4, 2, 2, 2, 4, false};
+    const bool wide = g.C % 64 == 0;
+    if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4, true};
+    return IgConfig{IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, wide ? 64 : 32, wide ? 2 : 4, false};
 }
 
 size_t ig_lds_bytes(const ConvGeom &g, int epi)
 {
     const IgConfig c = ig_config(g);
-    const size_t stage = (size_t)c.nstage * (c.bm() + c.bn()) * RB;
-    const size_t stg = std::max((size_t)c.bm() * 2 * c.bn(), (size_t)c.nw() * 64 * c.nj * 32 * 4);
+    const size_t stage = (size_t)c.nstage * (c.bm() + c.bn()) * 2 * c.bk;
+    const size_t scr = epi == EPI_STATS ? (size_t)c.nw() * 64 * c.nj * 32 * 4 : 0;
+    const size_t stg = std::max((size_t)c.bm() * 2 * c.bn(), scr);
     const size_t stats = epi == EPI_STATS ? (size_t)2 * g.K * 4 : 0;
     return (c.alias ? std::max(stage, stg) : stage + stg) + stats;
 }
 
-template <int MI, int NJ, int WGM, int WGN, int NSTAGE, int EPI, bool ALIAS>
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI, bool ALIAS>
 hipError_t ig_launch_one(const IgParams &prm, int grid, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const hipError_t e = hipFuncSetAttribute((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, NSTAGE, EPI, ALIAS>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e =
+        hipFuncSetAttribute((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI, ALIAS>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    return launch(conv_igemm_kernel<MI, NJ, WGM, WGN, NSTAGE, EPI, ALIAS>, dim3(grid), dim3(64 * WGM * WGN),
+    return launch(conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI, ALIAS>, dim3(grid), dim3(64 * WGM * WGN),
                   (uint32_t)lds, st, e0, e1, prm);
 }
 
-template <int MI, int NJ, int WGM, int WGN, int NSTAGE, bool ALIAS>
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, bool ALIAS>
 hipError_t ig_launch_cfg(int epi, const IgParams &prm, int grid, size_t lds, hipStream_t st, hipEvent_t e0,
                          hipEvent_t e1)
 {
     switch (epi) {
-    case EPI_STATS: return ig_launch_one<MI, NJ, WGM, WGN, NSTAGE, EPI_STATS, ALIAS>(prm, grid, lds, st, e0, e1);
+    case EPI_STATS: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_STATS, ALIAS>(prm, grid, lds, st, e0, e1);
     case EPI_BIAS_RELU:
-        return ig_launch_one<MI, NJ, WGM, WGN, NSTAGE, EPI_BIAS_RELU, ALIAS>(prm, grid, lds, st, e0, e1);
-    default: return ig_launch_one<MI, NJ, WGM, WGN, NSTAGE, EPI_PLAIN, ALIAS>(prm, grid, lds, st, e0, e1);
+        return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_BIAS_RELU, ALIAS>(prm, grid, lds, st, e0, e1);
+    default: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_PLAIN, ALIAS>(prm, grid, lds, st, e0, e1);
     }
 }
 
@@ -493,13 +528,12 @@ hipError_t ig_launch_cfg(int epi, const IgParams &prm, int grid, size_t lds, hip
 
 bool igemm_eligible(const ConvGeom &g, int epi)
 {
-    if (g.C % BK != 0 || g.M <= 0 || g.R > 16 || g.S > 16) return false;
+    if (g.C % 32 != 0 || g.M <= 0 || g.R > 16 || g.S > 16) return false;
     const IgConfig c = ig_config(g);
     if (g.K % c.bn() != 0) return false;
     if (c.alias && (ig_rows_per_wg(g) > c.bm() || g.K != c.bn())) return false;
-    // The multi-chunk form (256 x 128 chunks, one wave per SIMD) measured slower than the
-    // generic conv on the 28x28, 128-channel inference layer (174 vs 95 us); until that is
-    // understood only the single-chunk form is taken.
+    // The multi-chunk form measured slower than the generic conv on the 28x28, 128-channel
+    // inference layer (111 vs 83 us); until it is faster only the single-chunk form is taken.
     if (!c.alias) return false;
     const double xbytes = 2.0 * g.N * g.H * g.W * g.C, obytes = 2.0 * g.M * g.K, wbytes = 2.0 * g.K * g.Kg;
     if (xbytes >= 2147483648.0 || obytes >= 2147483648.0 || wbytes >= 2147483648.0) return false;
@@ -523,13 +557,17 @@ hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, cons
     prm.H = g.H; prm.W = g.W; prm.C = g.C; prm.K = g.K; prm.S = g.S;
     prm.sh = g.sh; prm.sw = g.sw; prm.ph = g.ph; prm.pw = g.pw;
     prm.P = g.P; prm.Q = g.Q; prm.M = g.M; prm.Kg = g.Kg;
-    prm.ksteps = g.Kg / BK;
+    prm.ksteps = g.Kg / c.bk;
     prm.rows_per_wg = ig_rows_per_wg(g);
     prm.ntn = g.K / c.bn();
     const int grid = ig_grid(g);
     const size_t lds = ig_lds_bytes(g, epi);
-    if (c.alias) return ig_launch_cfg<7, 1, 1, 8, 4, true>(epi, prm, grid, lds, st, e0, e1);
-    return ig_launch_cfg<4, 2, 2, 2, 4, false>(epi, prm, grid, lds, st, e0, e1);
+    if (c.alias) {
+        if (c.bk == 64) return ig_launch_cfg<7, 1, 1, 8, 64, 2, true>(epi, prm, grid, lds, st, e0, e1);
+        return ig_launch_cfg<7, 1, 1, 8, 32, 4, true>(epi, prm, grid, lds, st, e0, e1);
+    }
+    if (c.bk == 64) return ig_launch_cfg<IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, 64, 2, false>(epi, prm, grid, lds, st, e0, e1);
+    return ig_launch_cfg<IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, 32, 4, false>(epi, prm, grid, lds, st, e0, e1);
 }
 
 }  // namespace cbr
