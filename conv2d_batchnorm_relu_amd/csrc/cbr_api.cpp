@@ -84,7 +84,7 @@ InferLayout infer_layout(const ConvGeom &g)
 BwdLayout bwd_layout(const ConvGeom &g)
 {
     BwdLayout L;
-    const WgradPlan wp = wgrad_plan(g.M, g.K, g.Kg);
+    const WgradPlan wp = wgrad_plan(g);
     size_t o = 0;
     L.dz = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.M * g.K);
     L.part = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)bnbwd_blocks(g.M, g.K));

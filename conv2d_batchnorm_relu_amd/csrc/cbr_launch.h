@@ -76,11 +76,12 @@ int bnbwd_blocks(int M, int K);
 
 // Split factor of the weight-gradient reduction over output pixels.
 struct WgradPlan {
+    bool tr;          // transposed-read kernel (C % 128 == 0, K % 256 == 0)
     int bm, bn;       // tile over (K output channels) x (R*S*C)
     int tiles_m, tiles_n, splits;
     int rows_per_split;   // output pixels per split (multiple of the pixel step)
 };
-WgradPlan wgrad_plan(int M, int K, int Kg);
+WgradPlan wgrad_plan(const ConvGeom &g);
 
 // Persistent large-tile implicit-GEMM conv (C % 32 == 0, K a multiple of 128): at most
 // 256 workgroups, each over a contiguous range of output pixels; with EPI_STATS one

@@ -291,11 +291,244 @@ __global__ __launch_bounds__(NT) void flip_weights_kernel(const uint16_t *__rest
     }
 }
 
+
+// ---------------------------------------------------------------------------------
+// Transposed-read form (C % 128 == 0, K % 256 == 0): dz and im2col(x) slices are moved
+// into LDS unchanged (pixel rows, channels contiguous) by buffer-to-LDS loads, and the
+// MFMA fragments -- 8 consecutive pixels of one channel per lane -- come out of LDS with
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4a + b receives element b of the
+// 8-byte rows addressed by lanes a, a + 4, a + 8 and a + 12.  Lane i of a group therefore
+// addresses pixel (i / 4) at channel 4 (i % 4) of its 16-channel group, and lane 4a + b
+// ends up with channel 4a + b of four consecutive pixels; two such reads make one
+// fragment.  Rows are 512 (dz) or 256 (x) bytes; the 64-byte unit u of pixel row m sits
+// at unit u ^ (m % 4), so the four pixel rows of a read hit distinct banks.
+// The workgroup tile is 256 output channels x 128 filter positions (one tap, 128 input
+// channels), eight waves in a 4 x 2 grid of 64 x 64 wave tiles; the pixel range is split
+// over the grid's second dimension.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+struct WgradTrParams {
+    const uint16_t *dz, *x;
+    float *out;            // [splits][K][Kg] (dw itself when splits == 1)
+    int N, H, W, C, K, S, sh, sw, ph, pw, P, Q, M, Kg;
+    int rows_per_split;
+    FastDiv dpq, dq;
+};
+
+__device__ __forceinline__ i16x4 lds_tr16(uint32_t addr)
+{
+    i16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+template <int N>
+__device__ __forceinline__ void tr_lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" : : "i"(N) : "memory"); }
+template <int N>
+__device__ __forceinline__ void tr_vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory"); }
+__device__ __forceinline__ void tr_tie(i16x4 &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void tr_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    tr_lgkm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+// (A device function: the builtin has no host form.)
+__device__ __forceinline__ void tr_buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_u8 *dst, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 tr_join(i16x4 lo, i16x4 hi)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+constexpr int TR_BM = 256, TR_BN = 128, TR_WGM = 4, TR_WGN = 2, TR_NSTAGE = 3;
+constexpr int TR_NW = TR_WGM * TR_WGN, TR_NT = 64 * TR_NW;
+constexpr int TR_BKM = 64;                         // pixels per slice
+constexpr int TR_RSA = 2 * TR_BM, TR_RSB = 2 * TR_BN;   // row bytes of the dz and x slices
+constexpr int TR_STAGE_A = TR_BKM * TR_RSA, TR_STAGE = TR_STAGE_A + TR_BKM * TR_RSB;
+constexpr int TR_NA = TR_STAGE_A / 1024, TR_NINS = TR_STAGE / 1024;   // 1 KB load instructions
+constexpr int TR_IPW = TR_NINS / TR_NW;
+constexpr size_t TR_LDS = (size_t)TR_NSTAGE * TR_STAGE;
+static_assert(TR_NINS % TR_NW == 0, "load instructions per wave");
+
+__global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p)
+{
+    constexpr int MI = TR_BM / (32 * TR_WGM), NJ = TR_BN / (32 * TR_WGN);   // 2 x 2 blocks per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_u8 *)lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / TR_WGN, wn = wave % TR_WGN;
+    const int k0 = blockIdx.y * TR_BM, kk0 = blockIdx.x * TR_BN;
+    const int tap = kk0 / p.C, c0 = kk0 - tap * p.C;
+    const int tr = tap / p.S, ts = tap - tr * p.S;
+    const int m0 = blockIdx.z * p.rows_per_split;
+    const int m1 = min(p.M, m0 + p.rows_per_split);
+    const int nsteps = m1 > m0 ? (m1 - m0 + TR_BKM - 1) / TR_BKM : 0;
+    const __amdgpu_buffer_rsrc_t dzr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dz, 0, 2 * p.M * p.K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, 2 * p.N * p.H * p.W * p.C, 0x00020000);
+
+    // Slice loads of pixels mb .. mb + 63 into stage st: instruction u (wave u % NW) moves
+    // 1 KB of rows; lane l the 16 bytes at byte 16 l of it.
+    auto dma_issue = [&](int t) __attribute__((always_inline)) {
+        const int mb = m0 + t * TR_BKM;
+        const uint32_t st = (uint32_t)((t % TR_NSTAGE) * TR_STAGE);
+#pragma unroll
+        for (int q = 0; q < TR_IPW; ++q) {
+            const int u = wave + TR_NW * q;
+            if (u < TR_NA) {
+                const int row = u * (1024 / TR_RSA) + (16 * lane) / TR_RSA;
+                const int b = (16 * lane) % TR_RSA;
+                const int m = mb + row;
+                const int off = m < m1 ? 2 * (m * p.K + k0) + (b ^ ((row & 3) << 6)) : (int)OOB;
+                tr_buffer_load_lds16(dzr, (lds_u8 *)lds + st + u * 1024, off);
+            } else {
+                const int row = (u - TR_NA) * (1024 / TR_RSB) + (16 * lane) / TR_RSB;
+                const int b = (16 * lane) % TR_RSB;
+                const int m = mb + row;
+                const int n = (int)div_by((uint32_t)m, p.dpq), rem = m - n * p.P * p.Q;
+                const int pp = (int)div_by((uint32_t)rem, p.dq), q2 = rem - pp * p.Q;
+                const int h = pp * p.sh - p.ph + tr, w = q2 * p.sw - p.pw + ts;
+                const bool ok = m < m1 && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                const int off = ok ? 2 * (((n * p.H + h) * p.W + w) * p.C + c0) + (b ^ ((row & 3) << 6)) : (int)OOB;
+                tr_buffer_load_lds16(xr, (lds_u8 *)lds + st + u * 1024, off);
+            }
+        }
+    };
+
+    // Fragment addresses: lane l of group G = l / 16, i = l % 16 reads pixel
+    // 16 kh + 8 (G / 2) + 4 r + i / 4 at channel 16 (G % 2) + 4 (i % 4) of its block.
+    const int G = lane >> 4, li = lane & 15;
+    const int prow = 8 * (G >> 1) + (li >> 2);
+    uint32_t aa[MI], ba[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int byte = 2 * (wm * 32 * MI + 32 * i + 16 * (G & 1) + 4 * (li & 3));
+        aa[i] = lbase + prow * TR_RSA + (byte ^ ((prow & 3) << 6));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int byte = 2 * (wn * 32 * NJ + 32 * j + 16 * (G & 1) + 4 * (li & 3));
+        ba[j] = lbase + TR_STAGE_A + prow * TR_RSB + (byte ^ ((prow & 3) << 6));
+    }
+    i16x4 af[2][MI][2], bf[2][NJ][2];
+    auto read_frags = [&](i16x4 (&a)[MI][2], i16x4 (&b)[NJ][2], int t, int kh) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)((t % TR_NSTAGE) * TR_STAGE);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            a[i][0] = lds_tr16(aa[i] + so + (16 * kh) * TR_RSA);
+            a[i][1] = lds_tr16(aa[i] + so + (16 * kh + 4) * TR_RSA);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            b[j][0] = lds_tr16(ba[j] + so + (16 * kh) * TR_RSB);
+            b[j][1] = lds_tr16(ba[j] + so + (16 * kh + 4) * TR_RSB);
+        }
+    };
+    constexpr int NRD = 2 * (MI + NJ);   // reads per fragment set
+
+    f32x16 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    auto mfma = [&](const i16x4 (&a)[MI][2], const i16x4 (&b)[NJ][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_join(a[i][0], a[i][1]), tr_join(b[j][0], b[j][1]),
+                                                                    acc[i][j], 0, 0, 0);
+    };
+    auto tie_set = [&](i16x4 (&a)[MI][2], i16x4 (&b)[NJ][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) { tr_tie(a[i][0]); tr_tie(a[i][1]); }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) { tr_tie(b[j][0]); tr_tie(b[j][1]); }
+    };
+
+    // Slice t lives in stage t % 3; slices t + 1 and t + 2 are in flight while it is used.
+    const int npro = min(TR_NSTAGE - 1, nsteps);
+    for (int t = 0; t < npro; ++t) dma_issue(t);
+    if (nsteps > 0) {
+        if (npro > 1) tr_vm_wait<TR_IPW>();
+        else tr_vm_wait<0>();
+        tr_barrier();
+        read_frags(af[0], bf[0], 0, 0);
+    }
+    for (int t = 0; t < nsteps; ++t) {
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            read_frags(af[(kh + 1) & 1], bf[(kh + 1) & 1], t, kh + 1);
+            tr_lgkm_wait<NRD>();
+            tie_set(af[kh & 1], bf[kh & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(af[kh & 1], bf[kh & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kh == 0 && t + TR_NSTAGE - 1 < nsteps) dma_issue(t + TR_NSTAGE - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        tr_lgkm_wait<0>();
+        tie_set(af[1], bf[1]);
+        // slice t + 1 landed (slice t + 2 may stay in flight); every wave is past slice t
+        if (t + 2 < nsteps) tr_vm_wait<TR_IPW>();
+        else if (t + 1 < nsteps) tr_vm_wait<0>();
+        tr_barrier();
+        if (t + 1 < nsteps) read_frags(af[0], bf[0], t + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(af[1], bf[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Accumulator layout of v_mfma_f32_32x32x16: lane l holds column (l & 31) and rows
+    // 8*(v/4) + 4*(l >> 5) + v%4 of each 32 x 32 block.
+    float *out = p.out + (size_t)blockIdx.z * p.K * p.Kg;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int k = k0 + wm * 32 * MI + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int kk = kk0 + wn * 32 * NJ + 32 * j + (lane & 31);
+                out[(size_t)k * p.Kg + kk] = acc[i][j][v];
+            }
+}
+
+bool wgrad_tr_eligible(const ConvGeom &g)
+{
+    const double xbytes = 2.0 * g.N * g.H * g.W * g.C, zbytes = 2.0 * g.M * g.K;
+    return g.C % TR_BN == 0 && g.K % TR_BM == 0 && g.M > 0 && xbytes < 2147483648.0 && zbytes < 2147483648.0;
+}
+
 }  // namespace
 
-WgradPlan wgrad_plan(int M, int K, int Kg)
+WgradPlan wgrad_plan(const ConvGeom &g)
 {
+    const int M = g.M, K = g.K, Kg = g.Kg;
     WgradPlan p;
+    p.tr = wgrad_tr_eligible(g);
+    if (p.tr) {
+        // one workgroup per CU: 256 x 128 tiles, the pixel range split to fill the rest
+        p.bm = TR_BM;
+        p.bn = TR_BN;
+        p.tiles_m = K / TR_BM;
+        p.tiles_n = Kg / TR_BN;
+        const int tiles = p.tiles_m * p.tiles_n;
+        const int steps = (M + TR_BKM - 1) / TR_BKM;
+        const int want = std::max(1, std::min(steps, 256 / tiles));
+        const int steps_per = (steps + want - 1) / want;
+        p.rows_per_split = steps_per * TR_BKM;
+        p.splits = (M + p.rows_per_split - 1) / p.rows_per_split;
+        return p;
+    }
     p.bm = K >= 128 ? 128 : 64;
     p.bn = 128;
     p.tiles_m = (K + p.bm - 1) / p.bm;
@@ -313,7 +546,29 @@ WgradPlan wgrad_plan(int M, int K, int Kg)
 hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16_t *x, float *part, float *dw,
                              hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const WgradPlan p = wgrad_plan(g.M, g.K, g.Kg);
+    const WgradPlan p = wgrad_plan(g);
+    if (p.tr) {
+        WgradTrParams tp;
+        tp.dz = dz;
+        tp.x = x;
+        tp.out = p.splits == 1 ? dw : part;
+        tp.N = g.N; tp.H = g.H; tp.W = g.W; tp.C = g.C; tp.K = g.K; tp.S = g.S;
+        tp.sh = g.sh; tp.sw = g.sw; tp.ph = g.ph; tp.pw = g.pw; tp.P = g.P; tp.Q = g.Q; tp.M = g.M; tp.Kg = g.Kg;
+        tp.rows_per_split = p.rows_per_split;
+        tp.dpq = fast_div((uint32_t)(g.P * g.Q));
+        tp.dq = fast_div((uint32_t)g.Q);
+        hipError_t e = hipFuncSetAttribute((const void *)conv_wgrad_tr_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)TR_LDS);
+        if (e != hipSuccess) return e;
+        const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;
+        e = launch(conv_wgrad_tr_kernel, dim3(p.tiles_n, p.tiles_m, p.splits), dim3(TR_NT), (uint32_t)TR_LDS, st, e0,
+                   ek, tp);
+        if (e != hipSuccess || p.splits == 1) return e;
+        const long n = (long)g.K * g.Kg;
+        const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);
+        return launch(split_sum_kernel, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const float *)part, p.splits, n,
+                      dw);
+    }
     WgradParams prm{g, dz, x, p.splits == 1 ? dw : part, p.rows_per_split, fast_div((uint32_t)(g.P * g.Q)),
                     fast_div((uint32_t)g.Q)};
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);

@@ -157,6 +157,9 @@ BWD_GEOMS = [
     (Geometry(4, 14, 14, 64, 72, 1, 1, 1, 0), True),
     (Geometry(2, 12, 12, 128, 128, 3, 3, 1, 1), True),   # data gradient on 256 x 128 chunks
     (Geometry(3, 13, 11, 256, 64, 3, 3, 1, 1), True),    # data gradient: 64 -> 256 channels
+    (Geometry(2, 9, 11, 128, 512, 3, 3, 2, 1), False),   # transposed-read weight gradient: 2 x 9 tiles, stride 2
+    (Geometry(5, 12, 12, 128, 256, 1, 1, 1, 0), True),   # transposed-read weight gradient, 1x1, ragged pixel split
+    (Geometry(4, 48, 47, 128, 256, 3, 3, 1, 1), False),  # 6 slices per split, a 3-slice last split
 ]
 
 
