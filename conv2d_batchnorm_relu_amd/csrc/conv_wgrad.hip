@@ -374,33 +374,73 @@ __global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
         __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, 2 * p.N * p.H * p.W * p.C, 0x00020000);
 
     // Slice loads of pixels mb .. mb + 63 into stage st: instruction u (wave u % NW) moves
-    // 1 KB of rows; lane l the 16 bytes at byte 16 l of it.
+    // 1 KB of rows; lane l the 16 bytes at byte 16 l of it.  Instructions q < ZQ of a
+    // wave are dz rows, the others x rows.  A lane's pixel in an instruction advances by
+    // 64 per slice, so its decode (n, p, q) and x offset are kept per instruction and
+    // stepped with adds (64 = sa * Q + sb); multiply-high divisions per slice cost more
+    // than the loads themselves.
+    constexpr int ZQ = TR_NA / TR_NW;              // dz instructions per wave
+    constexpr int XQ = TR_IPW - ZQ;                // x instructions per wave
+    static_assert(TR_NA % TR_NW == 0, "dz and x instructions split per wave");
+    int zoff[ZQ];                                  // dz byte offset of the lane's row, current slice
+    int xm[XQ], xn[XQ], xp[XQ], xq[XQ], xoff[XQ];  // x row: pixel, its (n, p, q), byte offset
+    const int sa = TR_BKM / p.Q, sb = TR_BKM - sa * p.Q;
+#pragma unroll
+    for (int q = 0; q < ZQ; ++q) {
+        const int u = wave + TR_NW * q;
+        const int row = u * (1024 / TR_RSA) + (16 * lane) / TR_RSA;
+        const int b = (16 * lane) % TR_RSA;
+        zoff[q] = 2 * ((m0 + row) * p.K + k0) + (b ^ ((row & 3) << 6));
+    }
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int u = wave + TR_NW * (ZQ + q);
+        const int row = (u - TR_NA) * (1024 / TR_RSB) + (16 * lane) / TR_RSB;
+        const int b = (16 * lane) % TR_RSB;
+        const int m = m0 + row;
+        xm[q] = m;
+        xn[q] = (int)div_by((uint32_t)m, p.dpq);
+        const int rem = m - xn[q] * p.P * p.Q;
+        xp[q] = (int)div_by((uint32_t)rem, p.dq);
+        xq[q] = rem - xp[q] * p.Q;
+        xoff[q] = 2 * (((xn[q] * p.H + xp[q] * p.sh - p.ph + tr) * p.W + xq[q] * p.sw - p.pw + ts) * p.C + c0) +
+                  (b ^ ((row & 3) << 6));
+    }
+    // x offset steps: one column, one row wrap, one image wrap
+    const int dcol = 2 * p.sw * p.C, drow = 2 * (p.sh * p.W - p.Q * p.sw) * p.C;
+    const int dimg = 2 * (p.H - p.P * p.sh) * p.W * p.C;
     auto dma_issue = [&](int t) __attribute__((always_inline)) {
-        const int mb = m0 + t * TR_BKM;
         const uint32_t st = (uint32_t)((t % TR_NSTAGE) * TR_STAGE);
 #pragma unroll
-        for (int q = 0; q < TR_IPW; ++q) {
+        for (int q = 0; q < ZQ; ++q) {
             const int u = wave + TR_NW * q;
-            if (u < TR_NA) {
-                const int row = u * (1024 / TR_RSA) + (16 * lane) / TR_RSA;
-                const int b = (16 * lane) % TR_RSA;
-                const int m = mb + row;
-                const int off = m < m1 ? 2 * (m * p.K + k0) + (b ^ ((row & 3) << 6)) : (int)OOB;
-                tr_buffer_load_lds16(dzr, (lds_u8 *)lds + st + u * 1024, off);
-            } else {
-                const int row = (u - TR_NA) * (1024 / TR_RSB) + (16 * lane) / TR_RSB;
-                const int b = (16 * lane) % TR_RSB;
-                const int m = mb + row;
-                const int n = (int)div_by((uint32_t)m, p.dpq), rem = m - n * p.P * p.Q;
-                const int pp = (int)div_by((uint32_t)rem, p.dq), q2 = rem - pp * p.Q;
-                const int h = pp * p.sh - p.ph + tr, w = q2 * p.sw - p.pw + ts;
-                const bool ok = m < m1 && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-                const int off = ok ? 2 * (((n * p.H + h) * p.W + w) * p.C + c0) + (b ^ ((row & 3) << 6)) : (int)OOB;
-                tr_buffer_load_lds16(xr, (lds_u8 *)lds + st + u * 1024, off);
+            const int m = m0 + t * TR_BKM + u * (1024 / TR_RSA) + (16 * lane) / TR_RSA;
+            tr_buffer_load_lds16(dzr, (lds_u8 *)lds + st + u * 1024, m < m1 ? zoff[q] : (int)OOB);
+            zoff[q] += 2 * TR_BKM * p.K;
+        }
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int u = wave + TR_NW * (ZQ + q);
+            const int h = xp[q] * p.sh - p.ph + tr, w = xq[q] * p.sw - p.pw + ts;
+            const bool ok = xm[q] < m1 && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+            tr_buffer_load_lds16(xr, (lds_u8 *)lds + st + u * 1024, ok ? xoff[q] : (int)OOB);
+            // advance the pixel by 64: sa rows and sb columns, with wraps
+            xm[q] += TR_BKM;
+            xq[q] += sb;
+            xp[q] += sa;
+            xoff[q] += sb * dcol + sa * (drow + p.Q * dcol);
+            if (xq[q] >= p.Q) {
+                xq[q] -= p.Q;
+                ++xp[q];
+                xoff[q] += drow;
+            }
+            while (xp[q] >= p.P) {
+                xp[q] -= p.P;
+                ++xn[q];
+                xoff[q] += dimg;
             }
         }
     };
-
     // Fragment addresses: lane l of group G = l / 16, i = l % 16 reads pixel
     // 16 kh + 8 (G / 2) + 4 r + i / 4 at channel 16 (G % 2) + 4 (i % 4) of its block.
     const int G = lane >> 4, li = lane & 15;
