@@ -386,7 +386,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     };
 
     // ---- main loop over the slice sequence ----
-    const int npro = min(NSTAGE - 1, total);
+    // (with ALIAS the loads never run past the current chunk: its epilogue overwrites the
+    // slice buffers)
+    const int npro = min(NSTAGE - 1, ALIAS ? min(total, p.ksteps) : total);
     for (int g = 0; g < npro; ++g) dma_issue(g);
     if (total > 0) {
         vm_wait_steps<LMIN>(npro - 1);
@@ -397,8 +399,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     // One chunk's slices g0 .. g0 + ksteps - 1 with NB pixel blocks per wave; the MFMA
     // count is fixed for the whole chunk (the switch below picks the instance), so the
     // accumulators stay in place through the loop.
+    // With ALIAS the epilogue stages in the slice buffers, so loads stop at the chunk's end.
     auto chunk_loop = [&](auto nbc, int g0) __attribute__((always_inline)) {
         constexpr int NB = decltype(nbc)::value;
+        const int lim = ALIAS ? g0 + p.ksteps : total;   // slices loaded in this loop
         for (int ks = 0; ks < p.ksteps; ++ks) {
             const int g = g0 + ks;
             // k-steps 0 .. KH-2: read the next k-step's fragments, then the MFMAs of this one;
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
                 __builtin_amdgcn_sched_barrier(0);
                 mfma_set<MI, NJ, NB>(acc, af[kh & 1], bf[kh & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (kh == 0 && g + NSTAGE - 1 < total) dma_issue(g + NSTAGE - 1);
+                if (kh == 0 && g + NSTAGE - 1 < lim) dma_issue(g + NSTAGE - 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // last k-step: its fragments in, the next slice landed, every wave past this
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
             for (int j = 0; j < NJ; ++j) after_wait(af[(KH - 1) & 1][j]);
 #pragma unroll
             for (int i = 0; i < MI; ++i) after_wait(bf[(KH - 1) & 1][i]);
-            if (g + 1 < total) vm_wait_steps<LMIN>(min(NSTAGE - 2, total - 2 - g));
+            if (g + 1 < lim) vm_wait_steps<LMIN>(min(NSTAGE - 2, lim - 2 - g));
             barrier();
             if (ks + 1 < p.ksteps) read_frags(af[0], bf[0], g + 1, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -436,24 +440,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     };
     for (int c = 0; c < nchunk; ++c) {
         const int g0 = c * p.ksteps;
-        if constexpr (ALIAS) {
-            // single-chunk workgroups compute every block (a chunk of at most BM pixels;
-            // a partial block costs as much as a full one)
-            chunk_loop(std::integral_constant<int, MI>{}, g0);
-        } else {
-            const int mc = c / p.ntn;
-            const int nv = min(BM, r1 - (r0 + mc * BM)) - wm * 32 * MI;   // this wave's pixels
-            const int nbv = nv <= 0 ? 0 : min(MI, (nv + 31) / 32);
-            static_assert(MI <= 4, "block-count instances below");
-            if (nbv >= MI) chunk_loop(std::integral_constant<int, MI>{}, g0);
-            else if (nbv == 3) { if constexpr (MI > 3) chunk_loop(std::integral_constant<int, 3>{}, g0); }
-            else if (nbv == 2) { if constexpr (MI > 2) chunk_loop(std::integral_constant<int, 2>{}, g0); }
-            else if (nbv == 1) { if constexpr (MI > 1) chunk_loop(std::integral_constant<int, 1>{}, g0); }
-            else chunk_loop(std::integral_constant<int, 0>{}, g0);
-        }
+        // MFMA instances by this wave's pixel blocks in the chunk, rounded up to MI, 4, 2, 1
+        // or 0 (a partial block costs as much as a full one)
+        const int mc = c / p.ntn;
+        const int nv = min(BM, r1 - (r0 + mc * BM)) - wm * 32 * MI;
+        const int nbv = nv <= 0 ? 0 : min(MI, (nv + 31) / 32);
+        if (nbv > 4 || nbv == MI || (MI <= 4 && nbv > 2)) chunk_loop(std::integral_constant<int, MI>{}, g0);
+        else if (nbv > 2) { if constexpr (MI > 4) chunk_loop(std::integral_constant<int, 4>{}, g0); }
+        else if (nbv == 2) { if constexpr (MI > 2) chunk_loop(std::integral_constant<int, 2>{}, g0); }
+        else if (nbv == 1) { if constexpr (MI > 1) chunk_loop(std::integral_constant<int, 1>{}, g0); }
+        else chunk_loop(std::integral_constant<int, 0>{}, g0);
         epilogue(c);
         zero_acc();
-        if (g0 + p.ksteps < total) read_frags(af[0], bf[0], g0 + p.ksteps, 0);
+        if (g0 + p.ksteps < total) {
+            if constexpr (ALIAS) {
+                // the slice buffers held the staging tile: every wave is past its store
+                // reads before the next chunk's first slices load
+                barrier();
+                const int np = min(NSTAGE - 1, p.ksteps);
+                for (int g = 0; g < np; ++g) dma_issue(g0 + p.ksteps + g);
+                vm_wait_steps<LMIN>(np - 1);
+                barrier();
+            }
+            read_frags(af[0], bf[0], g0 + p.ksteps, 0);
+        }
     }
 
     if constexpr (EPI == EPI_STATS) {
@@ -462,12 +472,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         for (int i = tid; i < 2 * p.K; i += NT) p.partials[(size_t)blockIdx.x * 2 * p.K + i] = stat_acc[i];
     }
 }
-
-// Multi-chunk form: MI x NJ blocks per wave, WGM x WGN waves (256 x 128 chunks).
-#define IG_A_MI 4
-#define IG_A_NJ 2
-#define IG_A_WGM 2
-#define IG_A_WGN 2
 
 struct IgConfig {
     int mi, nj, wgm, wgn, bk, nstage;
@@ -481,14 +485,15 @@ int ig_grid(const ConvGeom &g) { return std::min(256, (g.M + 31) / 32); }
 int ig_rows_per_wg(const ConvGeom &g) { return (g.M + ig_grid(g) - 1) / ig_grid(g); }
 
 // K = 256 with at most 224 pixels per workgroup: one 224 x 256 chunk per workgroup, eight
-// waves side by side over the channels (two per SIMD); otherwise 256 x 128 chunks, four
-// waves in a 2 x 2 grid.  Slices of 64 reduction elements (whole 128-byte rows) when
-// C % 64 == 0, two in flight; else of 32, four in flight.
+// waves side by side over the channels (two per SIMD).  Otherwise chunks of 448 pixels x
+// 128 channels, eight waves in a 2 x 4 grid of 224 x 32 wave tiles.  Slices of 64
+// reduction elements (whole 128-byte rows) when C % 64 == 0, two in flight; else of 32,
+// four in flight.  The epilogue stages in the slice buffers.
 IgConfig ig_config(const ConvGeom &g)
 {
     const bool wide = g.C % 64 == 0;
     if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4, true};
-    return IgConfig{IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, wide ? 64 : 32, wide ? 2 : 4, false};
+    return IgConfig{7, 1, 2, 4, wide ? 64 : 32, wide ? 2 : 4, true};
 }
 
 size_t ig_lds_bytes(const ConvGeom &g, int epi)
@@ -531,10 +536,6 @@ bool igemm_eligible(const ConvGeom &g, int epi)
     if (g.C % 32 != 0 || g.M <= 0 || g.R > 16 || g.S > 16) return false;
     const IgConfig c = ig_config(g);
     if (g.K % c.bn() != 0) return false;
-    if (c.alias && (ig_rows_per_wg(g) > c.bm() || g.K != c.bn())) return false;
-    // The multi-chunk form measured slower than the generic conv on the 28x28, 128-channel
-    // inference layer (111 vs 83 us); until it is faster only the single-chunk form is taken.
-    if (!c.alias) return false;
     const double xbytes = 2.0 * g.N * g.H * g.W * g.C, obytes = 2.0 * g.M * g.K, wbytes = 2.0 * g.K * g.Kg;
     if (xbytes >= 2147483648.0 || obytes >= 2147483648.0 || wbytes >= 2147483648.0) return false;
     return ig_lds_bytes(g, epi) <= 160 * 1024;
@@ -562,12 +563,12 @@ hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, cons
     prm.ntn = g.K / c.bn();
     const int grid = ig_grid(g);
     const size_t lds = ig_lds_bytes(g, epi);
-    if (c.alias) {
+    if (c.wgm == 1) {
         if (c.bk == 64) return ig_launch_cfg<7, 1, 1, 8, 64, 2, true>(epi, prm, grid, lds, st, e0, e1);
         return ig_launch_cfg<7, 1, 1, 8, 32, 4, true>(epi, prm, grid, lds, st, e0, e1);
     }
-    if (c.bk == 64) return ig_launch_cfg<IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, 64, 2, false>(epi, prm, grid, lds, st, e0, e1);
-    return ig_launch_cfg<IG_A_MI, IG_A_NJ, IG_A_WGM, IG_A_WGN, 32, 4, false>(epi, prm, grid, lds, st, e0, e1);
+    if (c.bk == 64) return ig_launch_cfg<7, 1, 2, 4, 64, 2, true>(epi, prm, grid, lds, st, e0, e1);
+    return ig_launch_cfg<7, 1, 2, 4, 32, 4, true>(epi, prm, grid, lds, st, e0, e1);
 }
 
 }  // namespace cbr
