@@ -90,10 +90,9 @@ def test_train_forward_first_layer(g):
 
 # The persistent large-tile conv (C % 32 == 0, K a multiple of 128; at most 256
 # workgroups over contiguous pixel ranges).  K = 256 with at most 224 pixels per
-# workgroup runs one 224 x 256 chunk per workgroup (training forward, inference, data
-# gradient); the 256 x 128 multi-chunk form (several chunks per workgroup, a short last
-# chunk, several channel chunks) is switched off, and those shapes run the generic conv.
-# Also 1x1 / 5x5 / stride 2 and C = 96.
+# workgroup runs one 224 x 256 chunk per workgroup; everything else 448 x 128 chunks:
+# several chunks per workgroup, a short last chunk, several channel chunks, 1x1 / 5x5 /
+# stride 2, C = 96 (32-element slices).
 IGEMM_TRAIN_GEOMS = [
     Geometry(3, 13, 11, 64, 256, 3, 3, 1, 1),      # ragged ranges: 31 pixels per workgroup
     Geometry(256, 10, 20, 32, 256, 1, 1, 1, 0),    # 200 pixels per workgroup, one slice
