@@ -23,7 +23,8 @@
 // register staging): a wave's load instruction moves 8 pixels, and each lane fetches the
 // channel chunk that the permutation puts in its 16 bytes.  Each input row is read from
 // HBM once and serves all nine taps.  Row loads and z stores are issued from inside the
-// k-loops, one per k-step, rather than as a burst between steps.
+// k-loops, one per k-step, rather than as a burst between steps; the row loads come
+// from SIMD 3, which has the fewest pixel blocks per step.
 //
 // GEMM mapping: v_mfma_f32_32x32x16_bf16 with the filter as the A operand (32 output
 // channels) and the input pixels as the B operand (32 pixels), so each lane ends up
@@ -258,11 +259,9 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             *(u32x4 *)(lds + dst + ln * 16) = u32x4{0, 0, 0, 0};
         }
     };
-    // The memory waves (j == 0: waves 0..3, which win the MFMA arbitration against
-    // their SIMD partner and so have time to spare) issue the row loads.  A step's 1 KB z
-    // runs q = wave % 4 + 4 (4 half + k), k < 4, go out in two halves of up to four: half
-    // 0 from the memory waves, half 1 from the others.  load_staged reads a half of
-    // staging buffer buf into sd.
+    // A step's 1 KB z runs q = wave % 4 + 4 (4 half + k), k < 4, go out in two halves of
+    // up to four: half 0 from the waves of channel half 0, half 1 from the others.
+    // load_staged reads a half of staging buffer buf into sd.
     auto load_staged = [&](Staged &sd, int buf, int half, int ln, bool wait_now = true) {
         const uint8_t *sb = stg0 + buf * STG_BYTES;
 #pragma unroll
@@ -329,11 +328,14 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     prev.nq = 0;
     prev.zr = make_rsrc(p.z, 0);   // nothing staged yet: every store is dropped
     int pbuf = 1;
-    const bool memw = j == 0;                                 // a memory wave
+    const bool memw = j == 0;                                 // stores the first half of the z runs
+    // The input rows are loaded by the waves of SIMD 3, which has the fewest pixel
+    // blocks per step (7 blocks over 4 SIMDs).
+    constexpr int DMA_SIMD = NSIMD - 1;
     constexpr int DMA_T0 = 6;                                 // k-step of the first row load
-    constexpr int DMA_MAX = MAXW / 8;                          // row loads per memory wave
-    static_assert(TP == NSIMD, "one staged row per memory wave");
-    static_assert(DMA_T0 + DMA_MAX <= KSTEPS, "the row loads fit in one k-loop");
+    constexpr int DMA_MAX = MAXW / 8;                          // loads per row
+    static_assert(TP == 4, "two staged rows per wave of the loading SIMD");
+    static_assert(DMA_T0 + 2 * DMA_MAX <= KSTEPS, "the row loads fit in one k-loop");
     static_assert(2 * 4 * NSIMD * 1024 >= STG_BYTES, "two halves of runs cover a step");
     for (int img = 0; img < nimg; ++img) {
         const int n = (int)blockIdx.x + img * (int)gridDim.x;
@@ -355,20 +357,28 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             const int nblk = (npix + 31) >> 5;   // <= 7 (W <= 56)
             const int nb = (simd < nblk) + (simd + NSIMD < nblk);
             const bool full = npix == 32 * nblk;   // every pixel block complete
-            // The next step's rows p0 + 5 .. p0 + 8 stream into the 4 free slots, memory
-            // wave w loading row p0 + 5 + w (after an image's last step these rows are past
-            // its end: the slots get zeros, which nothing reads before the next image
-            // restages them).  Rows narrower than 7 loads repeat their last load.
+            // The next step's rows p0 + 5 .. p0 + 8 stream into the 4 free slots (after an
+            // image's last step these rows are past its end: the slots get zeros, which
+            // nothing reads before the next image restages them).
             const int h0n = p0 + TP + 1;
+            // k-step T's row load of the loading SIMD: wave j takes rows h0n + 2j and
+            // h0n + 2j + 1, one 8-pixel load per k-step (rows narrower than 7 loads repeat
+            // their last load)
+            auto row_part = [&](auto tc, int lt) {
+                constexpr int T = decltype(tc)::value;
+                constexpr int k = T - DMA_T0;
+                stage_part(n, h0n + 2 * j + k / DMA_MAX, min(k % DMA_MAX, ipr - 1), lt);
+            };
             const int cbuf = pbuf ^ 1;
             uint8_t *const stg = stg0 + cbuf * STG_BYTES;
-            // The previous step's z: the memory waves store the first half of its runs,
-            // the others the second half.
+            // The previous step's z: channel half 0's waves store the first half of its
+            // runs, the others the second half.
             load_staged(prev, pbuf, j, ln, false);   // waited for by the first store
             if (nb == 0) {   // no k-loop to carry the memory traffic
                 for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
-                if (memw)
-                    for (int k = 0; k < ipr; ++k) stage_part(n, h0n + wave, k, ln);
+                if (simd == DMA_SIMD)
+                    for (int r = 0; r < 2; ++r)
+                        for (int k = 0; k < ipr; ++k) stage_part(n, h0n + 2 * j + r, k, ln);
             }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
@@ -391,7 +401,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                 f32x16 acc;
                 if (memw && bb == 0) {
                     // k-steps 2..5: the first half of the previous step's z runs (its LDS
-                    // reads have landed by then); 6..: the row loads
+                    // reads have landed by then); 6..19 on SIMD 3: the row loads
                     auto side = [&](auto tc) {
                         constexpr int T = decltype(tc)::value;
                         // an opaque lane id per k-step keeps each instruction's address
@@ -400,16 +410,23 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                         asm volatile("" : "+v"(lt));
                         if constexpr (T >= 2 && T < 6) {
                             store_staged(prev, 0, T - 2, lt);
-                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + DMA_MAX) {
-                            stage_part(n, h0n + wave, min(T - DMA_T0, ipr - 1), lt);
+                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + 2 * DMA_MAX) {
+                            if (simd == DMA_SIMD) row_part(tc, lt);
                         }
                     };
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 } else if (bb == 0) {
-                    // k-steps 2..5: the second half of the previous step's z runs
+                    // k-steps 2..5: the second half of the previous step's z runs; 6..19 on
+                    // SIMD 3: the row loads
                     auto side = [&](auto tc) {
                         constexpr int T = decltype(tc)::value;
-                        if constexpr (T >= 2 && T < 6) store_staged(prev, 1, T - 2, ln);
+                        int lt = ln;
+                        asm volatile("" : "+v"(lt));
+                        if constexpr (T >= 2 && T < 6) {
+                            store_staged(prev, 1, T - 2, ln);
+                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + 2 * DMA_MAX) {
+                            if (simd == DMA_SIMD) row_part(tc, lt);
+                        }
                     };
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 } else {
