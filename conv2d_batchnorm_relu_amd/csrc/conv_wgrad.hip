@@ -264,10 +264,30 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
             }
 }
 
-// dw[i] = sum over splits s (in order) of part[s][i].
+// dw[i] = sum over splits s (in order) of part[s][i].  n % 4 == 0 takes 16-byte loads,
+// every split's load of a thread in flight at once.
 __global__ __launch_bounds__(NT) void split_sum_kernel(const float *__restrict__ part, int splits, long n,
                                                        float *__restrict__ dw)
 {
+    if ((n & 3) == 0) {
+        const long n4 = n >> 2;
+        const f32x4 *p4 = (const f32x4 *)part;
+        for (long i = (long)blockIdx.x * NT + threadIdx.x; i < n4; i += (long)gridDim.x * NT) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            int t = 0;
+            for (; t + 4 <= splits; t += 4) {
+                const f32x4 a = p4[(size_t)t * n4 + i], b = p4[(size_t)(t + 1) * n4 + i];
+                const f32x4 c = p4[(size_t)(t + 2) * n4 + i], d = p4[(size_t)(t + 3) * n4 + i];
+                s += a;
+                s += b;
+                s += c;
+                s += d;
+            }
+            for (; t < splits; ++t) s += p4[(size_t)t * n4 + i];
+            ((f32x4 *)dw)[i] = s;
+        }
+        return;
+    }
     for (long i = (long)blockIdx.x * NT + threadIdx.x; i < n; i += (long)gridDim.x * NT) {
         float s = 0.f;
         for (int t = 0; t < splits; ++t) s += part[(size_t)t * n + i];
