@@ -129,10 +129,10 @@ __device__ __forceinline__ void vm_wait_steps(int n)
     else vm_wait<0>();
 }
 
-// MI, NJ: pixel / channel blocks of 32 per wave; WGM x (4 / WGM) waves per workgroup.
-// ALIAS: every workgroup has at most one chunk, so the epilogue may reuse the slice
-// buffers; otherwise the staging tile has its own LDS.
-template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI, bool ALIAS>
+// MI, NJ: pixel / channel blocks of 32 per wave; WGM x WGN waves per workgroup; BK
+// reduction elements per slice, NSTAGE slices in flight.  The epilogue stages the output
+// tile (and the statistics) in the slice buffers, so a chunk's loads stop at its end.
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams p)
 {
     constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -147,11 +147,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     constexpr int LMIN = NINS / NW;               // per wave, at least
     constexpr int STAGE_B = ROWS * RB;
     constexpr int STG_ROW = 2 * BN;               // staging bytes per pixel
-    constexpr int STG_OFF = ALIAS ? 0 : NSTAGE * STAGE_B;
     constexpr int NF = NJ * 32;                   // statistics values per lane
     constexpr int SCR_B = EPI == EPI_STATS ? NW * 64 * NF * 4 : 0;   // statistics scratch
     static_assert(BN >= 128 && BM % 32 == 0 && (BK == 32 || BK == 64), "tile shape");
-    static_assert(!ALIAS || (NSTAGE * STAGE_B >= BM * STG_ROW && NSTAGE * STAGE_B >= SCR_B),
+    static_assert(NSTAGE * STAGE_B >= BM * STG_ROW && NSTAGE * STAGE_B >= SCR_B,
                   "the epilogue must fit the slice buffers");
 
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -160,7 +159,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int l32 = lane & 31, hi = lane >> 5;
     const int wm = wave / WGN, wn = wave % WGN;
-    float *stat_acc = (float *)(lds + (ALIAS ? NSTAGE * STAGE_B : NSTAGE * STAGE_B + std::max(BM * STG_ROW, SCR_B)));
+    float *stat_acc = (float *)(lds + NSTAGE * STAGE_B);
 
     const int r0 = blockIdx.x * p.rows_per_wg;
     const int r1 = min(p.M, r0 + p.rows_per_wg);
@@ -283,7 +282,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         const int mc = c / p.ntn, n0 = (c - mc * p.ntn) * BN;
         const int cm0 = r0 + mc * BM;
         const int nvalid = min(BM, r1 - cm0);
-        const uint32_t sbase = lbase + STG_OFF;
+        const uint32_t sbase = lbase;   // the staging tile occupies the slice buffers
         // An opaque copy of the lane id: the addresses below are then computed here, not
         // hoisted out of the main loop and held in registers through it.
         int ln = lane;
@@ -292,7 +291,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         if constexpr (EPI == EPI_STATS) {
             // Per lane: sums over its pixel blocks (pixels past the range are zeros);
             // then over the 32 pixel lanes and the WGM pixel-wave rows through LDS.
-            float *scr = (float *)(lds + STG_OFF);
+            float *scr = (float *)lds;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -386,9 +385,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     };
 
     // ---- main loop over the slice sequence ----
-    // (with ALIAS the loads never run past the current chunk: its epilogue overwrites the
-    // slice buffers)
-    const int npro = min(NSTAGE - 1, ALIAS ? min(total, p.ksteps) : total);
+    // (loads never run past the current chunk: its epilogue overwrites the slice buffers)
+    const int npro = min(NSTAGE - 1, min(total, p.ksteps));
     for (int g = 0; g < npro; ++g) dma_issue(g);
     if (total > 0) {
         vm_wait_steps<LMIN>(npro - 1);
@@ -399,10 +397,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     // One chunk's slices g0 .. g0 + ksteps - 1 with NB pixel blocks per wave; the MFMA
     // count is fixed for the whole chunk (the switch below picks the instance), so the
     // accumulators stay in place through the loop.
-    // With ALIAS the epilogue stages in the slice buffers, so loads stop at the chunk's end.
     auto chunk_loop = [&](auto nbc, int g0) __attribute__((always_inline)) {
         constexpr int NB = decltype(nbc)::value;
-        const int lim = ALIAS ? g0 + p.ksteps : total;   // slices loaded in this loop
+        const int lim = g0 + p.ksteps;   // the chunk's last slice bounds the loads
         for (int ks = 0; ks < p.ksteps; ++ks) {
             const int g = g0 + ks;
             // k-steps 0 .. KH-2: read the next k-step's fragments, then the MFMAs of this one;
@@ -453,15 +450,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         epilogue(c);
         zero_acc();
         if (g0 + p.ksteps < total) {
-            if constexpr (ALIAS) {
-                // the slice buffers held the staging tile: every wave is past its store
-                // reads before the next chunk's first slices load
-                barrier();
-                const int np = min(NSTAGE - 1, p.ksteps);
-                for (int g = 0; g < np; ++g) dma_issue(g0 + p.ksteps + g);
-                vm_wait_steps<LMIN>(np - 1);
-                barrier();
-            }
+            // the slice buffers held the staging tile: every wave is past its store reads
+            // before the next chunk's first slices load
+            barrier();
+            const int np = min(NSTAGE - 1, p.ksteps);
+            for (int g = 0; g < np; ++g) dma_issue(g0 + p.ksteps + g);
+            vm_wait_steps<LMIN>(np - 1);
+            barrier();
             read_frags(af[0], bf[0], g0 + p.ksteps, 0);
         }
     }
@@ -475,7 +470,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
 
 struct IgConfig {
     int mi, nj, wgm, wgn, bk, nstage;
-    bool alias;
     int bm() const { return 32 * mi * wgm; }
     int bn() const { return 32 * nj * wgn; }
     int nw() const { return wgm * wgn; }
@@ -492,8 +486,8 @@ int ig_rows_per_wg(const ConvGeom &g) { return (g.M + ig_grid(g) - 1) / ig_grid(
 IgConfig ig_config(const ConvGeom &g)
 {
     const bool wide = g.C % 64 == 0;
-    if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4, true};
-    return IgConfig{7, 1, 2, 4, wide ? 64 : 32, wide ? 2 : 4, true};
+    if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4};
+    return IgConfig{7, 1, 2, 4, wide ? 64 : 32, wide ? 2 : 4};
 }
 
 size_t ig_lds_bytes(const ConvGeom &g, int epi)
@@ -503,29 +497,29 @@ size_t ig_lds_bytes(const ConvGeom &g, int epi)
     const size_t scr = epi == EPI_STATS ? (size_t)c.nw() * 64 * c.nj * 32 * 4 : 0;
     const size_t stg = std::max((size_t)c.bm() * 2 * c.bn(), scr);
     const size_t stats = epi == EPI_STATS ? (size_t)2 * g.K * 4 : 0;
-    return (c.alias ? std::max(stage, stg) : stage + stg) + stats;
+    return std::max(stage, stg) + stats;
 }
 
-template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI, bool ALIAS>
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI>
 hipError_t ig_launch_one(const IgParams &prm, int grid, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const hipError_t e =
-        hipFuncSetAttribute((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI, ALIAS>,
+        hipFuncSetAttribute((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    return launch(conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI, ALIAS>, dim3(grid), dim3(64 * WGM * WGN),
+    return launch(conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI>, dim3(grid), dim3(64 * WGM * WGN),
                   (uint32_t)lds, st, e0, e1, prm);
 }
 
-template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, bool ALIAS>
+template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE>
 hipError_t ig_launch_cfg(int epi, const IgParams &prm, int grid, size_t lds, hipStream_t st, hipEvent_t e0,
                          hipEvent_t e1)
 {
     switch (epi) {
-    case EPI_STATS: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_STATS, ALIAS>(prm, grid, lds, st, e0, e1);
+    case EPI_STATS: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_STATS>(prm, grid, lds, st, e0, e1);
     case EPI_BIAS_RELU:
-        return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_BIAS_RELU, ALIAS>(prm, grid, lds, st, e0, e1);
-    default: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_PLAIN, ALIAS>(prm, grid, lds, st, e0, e1);
+        return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_BIAS_RELU>(prm, grid, lds, st, e0, e1);
+    default: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_PLAIN>(prm, grid, lds, st, e0, e1);
     }
 }
 
@@ -564,11 +558,11 @@ hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, cons
     const int grid = ig_grid(g);
     const size_t lds = ig_lds_bytes(g, epi);
     if (c.wgm == 1) {
-        if (c.bk == 64) return ig_launch_cfg<7, 1, 1, 8, 64, 2, true>(epi, prm, grid, lds, st, e0, e1);
-        return ig_launch_cfg<7, 1, 1, 8, 32, 4, true>(epi, prm, grid, lds, st, e0, e1);
+        if (c.bk == 64) return ig_launch_cfg<7, 1, 1, 8, 64, 2>(epi, prm, grid, lds, st, e0, e1);
+        return ig_launch_cfg<7, 1, 1, 8, 32, 4>(epi, prm, grid, lds, st, e0, e1);
     }
-    if (c.bk == 64) return ig_launch_cfg<7, 1, 2, 4, 64, 2, true>(epi, prm, grid, lds, st, e0, e1);
-    return ig_launch_cfg<7, 1, 2, 4, 32, 4, true>(epi, prm, grid, lds, st, e0, e1);
+    if (c.bk == 64) return ig_launch_cfg<7, 1, 2, 4, 64, 2>(epi, prm, grid, lds, st, e0, e1);
+    return ig_launch_cfg<7, 1, 2, 4, 32, 4>(epi, prm, grid, lds, st, e0, e1);
 }
 
 }  // namespace cbr
