@@ -74,28 +74,35 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
     const int h0 = 2 * p0 - p.ph;                   // input row of staged row 0
     const int W = p.W, Q = p.Q;
 
-    // Filter: R*4 16-byte chunks per output channel.
+    // The staging loops index with lane bit fields, not divisions: an integer division
+    // by a run-time value is some forty vector instructions.
+    // Filter: R*4 <= 32 16-byte chunks per output channel; lane bits 0..4 pick the chunk.
     {
-        const int cpr = p.R * 4;
-        for (int c = tid; c < KOUT * cpr; c += NT) {
-            const int k = c / cpr, ch = c - k * cpr;
-            *(u32x4 *)(wl + k * p.WRB + ch * 16) = ((const u32x4 *)p.wexp)[c];
-        }
+        const int cpr = p.R * 4, ch = tid & 31;
+        if (ch < cpr)
+            for (int k = tid >> 5; k < KOUT; k += NT / 32)
+                *(u32x4 *)(wl + k * p.WRB + ch * 16) = ((const u32x4 *)p.wexp)[k * cpr + ch];
     }
     // Input rows.  Zero: rows outside the image, and the columns left and right of the
-    // image (staged pixel j holds input column j - pw).  Image pixels: groups of 8
-    // (48 bytes = three 16-byte loads), widened to 8 bytes each.
+    // image (staged pixel j holds input column j - pw; at most 16 of them per row).  Image
+    // pixels: groups of 8 (48 bytes = three 16-byte loads), widened to 8 bytes each.
     const int gpr = W / 8;                          // pixel groups per row
-    for (int c = tid; c < NR * p.LW; c += NT) {
-        const int i = c / p.LW, j = c - i * p.LW;
-        const int h = h0 + i;
-        const bool inside = h >= 0 && h < p.H && j >= p.pw && j < p.pw + W;
-        if (!inside) *(u32x2 *)(xl + i * p.RB + j * 8) = u32x2{0u, 0u};
+    const int npad = p.LW - W;                      // zero columns per row, <= 16
+    for (int i = tid >> 4; i < NR; i += NT / 16) {
+        const int h = h0 + i, c = tid & 15;
+        if (h >= 0 && h < p.H) {
+            if (c < npad) {
+                const int j = c < p.pw ? c : W + c;
+                *(u32x2 *)(xl + i * p.RB + j * 8) = u32x2{0u, 0u};
+            }
+        } else {
+            for (int j = c; j < p.LW; j += 16) *(u32x2 *)(xl + i * p.RB + j * 8) = u32x2{0u, 0u};
+        }
     }
-    for (int c = tid; c < NR * gpr; c += NT) {
-        const int i = c / gpr, gi = c - i * gpr;
+    for (int i = tid >> 5; i < NR; i += NT / 32) {
         const int h = h0 + i;
         if (h < 0 || h >= p.H) continue;
+        for (int gi = tid & 31; gi < gpr; gi += 32) {
         const u32x4 *src = (const u32x4 *)(p.x + (((size_t)n * p.H + h) * W + 8 * gi) * 3);
         const u32x4 a = src[0], b = src[1], d = src[2];
         const uint32_t v[12] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], d[0], d[1], d[2], d[3]};
@@ -107,6 +114,7 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
             const uint32_t lo = half(3 * e) | (half(3 * e + 1) << 16);
             *(u32x2 *)(dst + e * 8) = u32x2{lo, half(3 * e + 2)};
         }
+        }
     }
     __syncthreads();
 
@@ -116,10 +124,14 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
     const int wa = (32 * j + l32) * p.WRB + hi * 16;
     int xa[UPW];
     bool valid[UPW];
+    const float invQ = 1.0f / (float)Q;
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
         const int pi = 32 * (blk0 + u) + l32;           // pixel within the band
-        const int pr = pi / Q, q = pi - pr * Q;
+        int pr = (int)((float)pi * invQ);               // pi / Q, corrected below
+        pr -= pr * Q > pi;
+        pr += (pr + 1) * Q <= pi;
+        const int q = pi - pr * Q;
         valid[u] = pr < TP && p0 + pr < p.P;
         xa[u] = valid[u] ? KOUT * p.WRB + 2 * pr * p.RB + 2 * q * 8 + hi * 16 : KOUT * p.WRB;
     }
@@ -243,7 +255,8 @@ bool c3s2_eligible(const ConvGeom &g)
     // 14 pixel blocks of 32 must cover TP output rows; the filter row (R taps of 8 x 4)
     // and the staged rows must fit LDS with two workgroups per CU.
     return g.C == 3 && g.K == KOUT && g.sh == 2 && g.sw == 2 && g.R >= 1 && g.R <= 7 && g.S >= 1 && g.S <= 8 &&
-           g.W % 8 == 0 && TP * g.Q <= 32 * NBLK && (g.pw % 2) == 1 && c3s2_lds_bytes(g) <= 80 * 1024 &&
+           g.W % 8 == 0 && TP * g.Q <= 32 * NBLK && (g.pw % 2) == 1 && c3_lw(g) - g.W <= 16 &&
+           c3s2_lds_bytes(g) <= 80 * 1024 &&
            (size_t)g.N * g.P * g.Q * KOUT * 2 < 0x7fffffffu;
 }
 
