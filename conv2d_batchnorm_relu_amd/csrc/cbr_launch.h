@@ -52,7 +52,7 @@ ConvPlan conv_plan(const ConvGeom &g);
 
 // Persistent 3x3 / stride 1 / pad 1, 64 -> 64 channel convolution + channel statistics.
 constexpr int HALO_MAX_GRID = 256;                        // one workgroup per MI355X CU
-constexpr int HALO_MAX_LDS = 10 * (56 + 2) * 128 + 3 * 4 * 56 * 128;   // input-row ring + 3 z staging buffers, W <= 56
+constexpr int HALO_MAX_LDS = 160 * 1024;                  // the whole LDS of a CU
 bool halo_eligible(const ConvGeom &g);
 int halo_grid(const ConvGeom &g);
 size_t halo_lds_bytes(const ConvGeom &g);

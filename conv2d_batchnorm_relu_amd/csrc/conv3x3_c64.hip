@@ -4,18 +4,20 @@
 // page's training forward, section 4.1).
 //
 // One 512-thread workgroup per compute unit (two waves per SIMD) walks whole images in
-// steps of TP = 4 output rows.
+// steps of SP = 256 output pixels (8 blocks of 32) in NHWC order, regardless of where
+// image rows begin, so that every SIMD has exactly two pixel blocks per full step.
 //   - Wave w computes output channels 32j .. 32j + 31, j = w / 4, and keeps that half of
 //     the filter, 32 x 576 bf16, in registers (36 MFMA operand fragments, 144 VGPRs), so
 //     LDS only serves input pixels.  Waves w and w + 4 share a SIMD and the same pixel
 //     blocks: the SIMD holds both channel halves of its blocks.
-//   - LDS holds a ring of 10 input rows: the 6 rows a step reads (its output rows +-1)
-//     and the 4 rows of the next step, which stream in while the step computes.  Row h
-//     (-1 <= h <= H) lives in slot (h + 1) % 10; the padding rows -1 and H are zero slots.
-//     A slot holds W + 2 pixels of 64 channels (zero columns at both ends), 128 bytes
-//     each, whose eight 16-byte channel chunks are stored XOR-permuted by (pixel / 2) % 8,
-//     so that 16 consecutive pixels of one fragment read hit 16 distinct 4-bank groups.
-//   - Two staging buffers for a step's z (224 pixels x 128 bytes): the epilogues write
+//   - LDS holds a ring of input rows: the rows a step reads (its output rows +-1) and
+//     the rows the next step adds, which stream in while the step computes.  Row h
+//     (-1 <= h <= H) lives in slot (h + 1) % nslot; the padding rows -1 and H are zero
+//     slots.  A slot holds W + 2 pixels of 64 channels (zero columns at both ends), 128
+//     bytes each, whose eight 16-byte channel chunks are stored XOR-permuted by
+//     (pixel / 2) % 8, so that 16 consecutive pixels of one fragment read hit 16 distinct
+//     4-bank groups.
+//   - Two staging buffers for a step's z (256 pixels x 128 bytes): the epilogues write
 //     one; during the next step every wave stores a share of it as whole 1 KB runs of
 //     pixel rows, which costs the memory pipeline a quarter of the cache-line
 //     operations of storing straight from the MFMA layout.
@@ -23,13 +25,12 @@
 // register staging): a wave's load instruction moves 8 pixels, and each lane fetches the
 // channel chunk that the permutation puts in its 16 bytes.  Each input row is read from
 // HBM once and serves all nine taps.  Row loads and z stores are issued from inside the
-// k-loops, one per k-step, rather than as a burst between steps; the row loads come
-// from SIMD 3, which has the fewest pixel blocks per step.
+// k-loops, one per k-step, rather than as a burst between steps.
 //
 // GEMM mapping: v_mfma_f32_32x32x16_bf16 with the filter as the A operand (32 output
 // channels) and the input pixels as the B operand (32 pixels), so each lane ends up
-// holding 4 consecutive output channels of one pixel.  A step has TP*W/32 pixel blocks
-// (7 for W = 56); the waves on SIMD s take blocks s and s + 4.
+// holding 4 consecutive output channels of one pixel.  The waves on SIMD s take blocks
+// s and s + 4 of a step.
 // The statistics are accumulated per lane in fp32 registers across the whole persistent
 // loop and reduced across lanes and waves once at the end: one partial per workgroup.
 #include <hip/hip_ext.h>
@@ -41,17 +42,20 @@ namespace {
 
 constexpr int HC = 64;                  // input channels
 constexpr int HK = 64;                  // output channels
-constexpr int TP = 4;                   // output rows per step
-constexpr int NSLOT = 10;               // ring slots: TP + 2 read, TP incoming
+constexpr int SP = 256;                 // output pixels per step
 constexpr int PXB = HC * 2;             // bytes per staged pixel
 constexpr int NT = 512;                 // threads: 8 waves, two per SIMD
 constexpr int NW = NT / 64;
 constexpr int NSIMD = 4;
 constexpr int MAXW = 56;
 constexpr int KSTEPS = 36;              // 9 taps x 4 chunks of 16 input channels
-constexpr int STG_BYTES = TP * MAXW * PXB;   // one step's z, pixel-major
+constexpr int STG_BYTES = SP * PXB;     // one step's z, pixel-major
 constexpr int STATS_BYTES = 16 * NT * 4;     // final cross-lane reduction area
 constexpr int FILTER_BYTES = HK * 72 * 16;    // the filter, staged once through LDS
+// Row loads per wave per step: a step adds at most ceil(SP / W) input rows of W / 8
+// loads each, i.e. at most SP / 8 + W / 8 <= 39 loads over the 8 waves.
+constexpr int LPW = 5;
+static_assert(NW * LPW >= SP / 8 + MAXW / 8, "row loads per step");
 
 struct HaloParams {
     const uint16_t *x;
@@ -60,17 +64,27 @@ struct HaloParams {
     float *partials;       // [gridDim.x][2][64]
     int N, H, W;
     int slot_bytes;        // (W + 2) * PXB
-    uint32_t invW;         // ceil(65536 / W): v / W == (v * invW) >> 16 for v * W <= 65536
+    int nslot;             // ring slots: >= the rows a step reads plus the rows the next adds
+    uint32_t mW;           // ceil(2^32 / W): v / W == mulhi(v, mW) for v < 2^32 / W
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ int div_w(int v, uint32_t invW) { return (int)(((uint32_t)v * invW) >> 16); }
+__device__ __forceinline__ int div_w(int v, uint32_t mW) { return (int)__umulhi((uint32_t)v, mW); }
 
-// Chunk permutation of staged pixel u: channel chunk c is stored at position c ^ perm(u).
+// Chunk permutation of staged pixel u (of a z staging row, or of input row h together
+// with row_flip): channel chunk c is stored at position c ^ perm(u) (^ row_flip(h)).
 __device__ __forceinline__ int perm(int u) { return (u >> 1) & 7; }
+
+// The input-row permutation continues across rows as if the rows were one run of pixels:
+// pixel u of row h is permuted like pixel u + (h + 1) W of one long row, i.e. by
+// perm(u) ^ row_flip(h), the flip 4 ((h + 1) W / 8 mod 2) (W a multiple of 8).  A pixel
+// block that spans two rows then reads 32 consecutive permutation positions, as one
+// inside a row does; with a plain per-row permutation the two rows' positions repeat and
+// every read of such a block takes twice as long.
+__device__ __forceinline__ int row_flip(int h, int ipr) { return (((h + 1) * ipr) & 1) << 2; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
 {
@@ -79,11 +93,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 
 // Per pixel block: LDS address of the lane's staged pixel q in the slot of tap row r
 // (rb[r]), and the lane's chunk permutation of pixels q + sx, pre-shifted and with the
-// lane's k-half folded in (cx[sx] = (hi ^ perm(q + sx)) << 4): the fragment of tap
-// (r, sx), 16-channel chunk kc is at rb[r] + 128 sx + ((32 * kc) ^ cx[sx]).
+// lane's k-half folded in (cx[f][sx] = (hi ^ perm(q + sx) ^ row_flip(h)) << 4, f = 1 for
+// the middle tap row, whose flip differs from the other two): the fragment of tap
+// (r, sx), 16-channel chunk kc is at rb[r] + 128 sx + ((32 * kc) ^ cx[r == 1][sx]).
 struct BlockAddr {
     int rb[3];
-    int cx[3];
+    int cx[2][3];
 };
 
 // LDS fragment reads in inline assembly, with explicit waits.  While global-to-LDS loads
@@ -126,7 +141,7 @@ struct KLoop {
     __device__ __forceinline__ void read()
     {
         constexpr int tap = T >> 2, kc = T & 3, r = tap / 3, sx = tap - 3 * r;
-        xf[T % KD] = lds_read16<128 * sx>(ba.rb[r] + ((32 * kc) ^ ba.cx[sx]));
+        xf[T % KD] = lds_read16<128 * sx>(ba.rb[r] + ((32 * kc) ^ ba.cx[r == 1][sx]));
     }
 
     template <int T>
@@ -216,59 +231,50 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int simd = wave & (NSIMD - 1), j = wave >> 2;
-    const int H = p.H, W = p.W, SLOT = p.slot_bytes;
-    const uint32_t invW = p.invW;
-    const int spi = (H + TP - 1) / TP;                        // steps per image
+    const int H = p.H, W = p.W, SLOT = p.slot_bytes, NSLOT = p.nslot;
+    const uint32_t mW = p.mW;
+    const int HW = H * W;
+    const int spi = (HW + SP - 1) / SP;                       // steps per image
     const int nimg = (p.N - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int hi = lane >> 5;                                 // k-half of the MFMA operands
     const int l32 = lane & 31;
     const int ipr = W / 8;                                    // 8-pixel load instructions per row
     const uint32_t lbase = (uint32_t)(uintptr_t)(lds_u8 *)lds;
     uint8_t *const stg0 = lds + NSLOT * SLOT;                 // two step staging buffers
+    // Input rows -1 .. rows0 - 2 are the first step's: its output rows 0 .. last +- 1.
+    const int rows0 = div_w(min(SP, HW) - 1, mW) + 3;
 
-    // Staging of input rows h0 .. h0 + nrows - 1 (each -1 <= h <= H + 3) of image n into
-    // their slots: image rows by global-to-LDS loads, the others as zeros.  Instruction
-    // gi (row ri = gi / ipr, pixels 8i .. 8i+7) is issued by wave gi % 8; lane l moves
-    // pixel 8i + l/8, position l % 8, which holds channel chunk (l % 8) ^ perm(1 + 8i + l/8).
-    auto stage_one = [&](int n, int h0, int gi, int ln) {
-        const int ri = gi / ipr, i = gi - ri * ipr;
-        const int h = h0 + ri;
-        const int dst = ((h + 1) % NSLOT) * SLOT + (1 + 8 * i) * PXB;   // wave-uniform
-        if (h >= 0 && h < H) {
-            const int u = 1 + 8 * i + (ln >> 3);
-            const uint16_t *src =
-                p.x + ((size_t)(n * H + h) * W + 8 * i + (ln >> 3)) * HC + (((ln & 7) ^ perm(u)) * 8);
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_u8 *)lds + dst, 16, 0, 0);
-        } else {
-            *(u32x4 *)(lds + dst + ln * 16) = u32x4{0, 0, 0, 0};
-        }
-    };
-    auto stage_rows = [&](int n, int h0, int nrows) {
-        for (int gi = wave; gi < nrows * ipr; gi += NW) stage_one(n, h0, gi, lane);
-    };
-    // Load k (pixels 8k .. 8k + 7) of input row h of image n into its slot, for the
-    // row-per-memory-wave staging inside the k-loops (k < ipr).
+    // Load k (pixels 8k .. 8k + 7) of input row h (-1 <= h <= H) of image n into its slot:
+    // an image row by a global-to-LDS load, the padding rows as zeros.  Lane l moves pixel
+    // 8k + l/8, position l % 8, which holds channel chunk (l % 8) ^ perm(1 + 8k + l/8).
     auto stage_part = [&](int n, int h, int k, int ln) {
         const int dst = ((h + 1) % NSLOT) * SLOT + (1 + 8 * k) * PXB;   // wave-uniform
         if (h >= 0 && h < H) {
             const int u = 1 + 8 * k + (ln >> 3);
             const uint16_t *src =
-                p.x + ((size_t)(n * H + h) * W + 8 * k + (ln >> 3)) * HC + (((ln & 7) ^ perm(u)) * 8);
+                p.x + ((size_t)(n * H + h) * W + 8 * k + (ln >> 3)) * HC + (((ln & 7) ^ perm(u) ^ row_flip(h, ipr)) * 8);
             __builtin_amdgcn_global_load_lds((const void *)src, (lds_u8 *)lds + dst, 16, 0, 0);
         } else {
             *(u32x4 *)(lds + dst + ln * 16) = u32x4{0, 0, 0, 0};
         }
     };
+    // Rows h0 .. h0 + nrows - 1 of image n: load gi (row gi / ipr, pixels 8 (gi % ipr) ..)
+    // is issued by wave gi % 8.  gi / ipr == 8 gi / W.
+    auto stage_rows = [&](int n, int h0, int nrows) {
+        for (int gi = wave; gi < nrows * ipr; gi += NW) {
+            const int ri = div_w(8 * gi, mW);
+            stage_part(n, h0 + ri, gi - ri * ipr, lane);
+        }
+    };
     // A step's 1 KB z runs q = wave % 4 + 4 (4 half + k), k < 4, go out in two halves of
-    // up to four: half 0 from the waves of channel half 0, half 1 from the others.
+    // four: half 0 from the waves of channel half 0, half 1 from the others.
     // load_staged reads a half of staging buffer buf into sd.
     auto load_staged = [&](Staged &sd, int buf, int half, int ln, bool wait_now = true) {
         const uint8_t *sb = stg0 + buf * STG_BYTES;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int px = 8 * (simd + NSIMD * (4 * half + k)) + (ln >> 3);
-            const int pxc = px < TP * MAXW ? px : 0;   // runs past nq are not stored
-            sd.d[k] = *(const u32x4 *)(sb + pxc * PXB + (((ln & 7) ^ perm(pxc)) << 4));
+            const int px = 8 * (simd + NSIMD * (4 * half + k)) + (ln >> 3);   // < SP
+            sd.d[k] = *(const u32x4 *)(sb + px * PXB + (((ln & 7) ^ perm(px)) << 4));
         }
         // A use here makes the compiler wait for the reads now, not at the first store
         // inside the k-loop, where its wait would also drain the k-loop's read-ahead.
@@ -286,21 +292,22 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     };
 
     // The filter half into registers, through LDS: global-to-LDS loads put 16-byte chunk
-    // c of filter row r (KRSC: 72 chunks per output channel) at F + (64c + r) * 16, in the
-    // ring slots 6.. and the staging buffers, which the first k-loop does not touch yet.
-    // Load c gathers chunk c of all 64 rows (lane r), so the fragment reads below are
-    // conflict-free.  Fragment t of lane (l32, hi) is output channel 32j + l32, tap t / 4,
-    // input channels 16 (t % 4) + 8 hi .. + 7: chunk 8 (t / 4) + 2 (t % 4) + hi.  Meanwhile
-    // the first image's rows -1..4 stream into slots 0..5.
-    const int F = 6 * SLOT;
+    // c of filter row r (KRSC: 72 chunks per output channel) at F + (64c + r) * 16, past
+    // the first step's ring slots (in slots the first k-loop has not loaded yet and in
+    // the staging buffers).  Load c gathers chunk c of all 64 rows (lane r), so the
+    // fragment reads below are conflict-free.  Fragment t of lane (l32, hi) is output
+    // channel 32j + l32, tap t / 4, input channels 16 (t % 4) + 8 hi .. + 7: chunk
+    // 8 (t / 4) + 2 (t % 4) + hi.  Meanwhile the first image's first rows stream into
+    // slots 0 .. rows0 - 1.
+    const int F = rows0 * SLOT;
     for (int c = wave; c < 72; c += NW)
         __builtin_amdgcn_global_load_lds((const void *)(p.w + ((size_t)lane * 72 + c) * 8), (lds_u8 *)lds + F + c * 1024,
                                          16, 0, 0);
-    for (int c = tid; c < 6 * 16; c += NT) {
+    for (int c = tid; c < rows0 * 16; c += NT) {
         const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
         *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
     }
-    if (nimg > 0) stage_rows(blockIdx.x, -1, TP + 2);
+    if (nimg > 0) stage_rows(blockIdx.x, -1, rows0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     bf16x8 wf[KSTEPS];
@@ -309,10 +316,10 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
         wf[t] = *(const bf16x8 *)(lds + F + (((t >> 2) * 8 + (t & 3) * 2 + hi) * 64 + 32 * j + l32) * 16);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // the filter area is free again
-    // The padding columns of slots 6..9 zeroed (the first k-loop's row loads fill the
+    // The padding columns of the other slots zeroed (the k-loops' row loads fill the
     // other columns).
-    for (int c = tid; c < 4 * 16; c += NT) {
-        const int slot = 6 + (c >> 4), col = (c & 8) ? W + 1 : 0;
+    for (int c = rows0 * 16 + tid; c < NSLOT * 16; c += NT) {
+        const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
         *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
     }
 
@@ -328,20 +335,14 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     prev.nq = 0;
     prev.zr = make_rsrc(p.z, 0);   // nothing staged yet: every store is dropped
     int pbuf = 1;
-    const bool memw = j == 0;                                 // stores the first half of the z runs
-    // The input rows are loaded by the waves of SIMD 3, which has the fewest pixel
-    // blocks per step (7 blocks over 4 SIMDs).
-    constexpr int DMA_SIMD = NSIMD - 1;
     constexpr int DMA_T0 = 6;                                 // k-step of the first row load
-    constexpr int DMA_MAX = MAXW / 8;                          // loads per row
-    static_assert(TP == 4, "two staged rows per wave of the loading SIMD");
-    static_assert(DMA_T0 + 2 * DMA_MAX <= KSTEPS, "the row loads fit in one k-loop");
-    static_assert(2 * 4 * NSIMD * 1024 >= STG_BYTES, "two halves of runs cover a step");
+    static_assert(DMA_T0 + LPW <= KSTEPS, "the row loads fit in one k-loop");
+    static_assert(2 * 4 * NSIMD * 1024 == STG_BYTES, "two halves of runs cover a step");
     for (int img = 0; img < nimg; ++img) {
         const int n = (int)blockIdx.x + img * (int)gridDim.x;
         if (img > 0) {
-            // A new image: every wave is past the last step's reads; restage rows -1..4.
-            stage_rows(n, -1, TP + 2);
+            // A new image: every wave is past the last step's reads; restage its first rows.
+            stage_rows(n, -1, rows0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -351,57 +352,84 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int l32s = ln & 31, his = ln >> 5;
-            const int p0 = s * TP;
-            const int rows_s = min(TP, H - p0);
-            const int npix = rows_s * W;
-            const int nblk = (npix + 31) >> 5;   // <= 7 (W <= 56)
+            const int a = s * SP;                               // first pixel of the step
+            const int npix = min(SP, HW - a);
+            const int nblk = (npix + 31) >> 5;                  // <= 8
             const int nb = (simd < nblk) + (simd + NSIMD < nblk);
-            const bool full = npix == 32 * nblk;   // every pixel block complete
-            // The next step's rows p0 + 5 .. p0 + 8 stream into the 4 free slots (after an
-            // image's last step these rows are past its end: the slots get zeros, which
-            // nothing reads before the next image restages them).
-            const int h0n = p0 + TP + 1;
-            // k-step T's row load of the loading SIMD: wave j takes rows h0n + 2j and
-            // h0n + 2j + 1, one 8-pixel load per k-step (rows narrower than 7 loads repeat
-            // their last load)
+            const bool full = npix == 32 * nblk;                // every pixel block complete
+            const int ofr = div_w(a, mW);                       // first output row of the step
+            const int olr = div_w(a + npix - 1, mW);            // last output row
+            const int fslot = ofr % NSLOT;                      // slot of input row ofr - 1
+            // The next step's new input rows olr + 2 .. olr1 + 1 (none after the image's
+            // last step) stream into their slots: load gi of them (row olr + 2 + gi / ipr,
+            // pixels 8 (gi % ipr) ..) goes to wave gi % 8 at k-step DMA_T0 + gi / 8.  The
+            // rows below H are contiguous in x, so load gi reads bytes 1024 gi .. of them;
+            // row H (the bottom padding) is written as zeros.
+            int nload = 0, nmem = 0;
+            if (s + 1 < spi) {
+                const int a1 = a + SP;
+                const int olr1 = div_w(a1 + min(SP, HW - a1) - 1, mW);
+                nload = (olr1 - olr) * ipr;
+                nmem = max(0, min(olr1, H - 2) - olr) * ipr;
+            }
+            const int slot_a = (olr + 3) % NSLOT;                // slot of input row olr + 2
+            const uint16_t *const xa = p.x + ((size_t)n * H + olr + 2) * W * HC;
             auto row_part = [&](auto tc, int lt) {
-                constexpr int T = decltype(tc)::value;
-                constexpr int k = T - DMA_T0;
-                stage_part(n, h0n + 2 * j + k / DMA_MAX, min(k % DMA_MAX, ipr - 1), lt);
+                constexpr int t = decltype(tc)::value - DMA_T0;
+                const int gi = wave + NW * t;                   // wave-uniform
+                if (gi < nload) {
+                    const int ri = div_w(8 * gi, mW);
+                    const int k = gi - ri * ipr;
+                    int sl = slot_a + ri;
+                    if (sl >= NSLOT) sl -= NSLOT;
+                    const int dst = sl * SLOT + (1 + 8 * k) * PXB;
+                    if (gi < nmem) {
+                        // lane l: pixel 8k + l/8, position l % 8, which holds channel chunk
+                        // (l % 8) ^ perm(1 + 8k + l/8) ^ row_flip(h)
+                        //   = (l % 8) ^ ((1 + l/8) / 2) ^ 4 (k % 2) ^ row_flip(h)
+                        const int l8 = lt >> 3;
+                        const int off = (l8 * HC + (((lt & 7) ^ ((1 + l8) >> 1)) << 3)) ^
+                                        (((k & 1) << 5) ^ (row_flip(olr + 2 + ri, ipr) << 3));
+                        __builtin_amdgcn_global_load_lds((const void *)(xa + gi * 512 + off), (lds_u8 *)lds + dst,
+                                                         16, 0, 0);
+                    } else {
+                        *(u32x4 *)(lds + dst + lt * 16) = u32x4{0, 0, 0, 0};
+                    }
+                }
             };
             const int cbuf = pbuf ^ 1;
             uint8_t *const stg = stg0 + cbuf * STG_BYTES;
             // The previous step's z: channel half 0's waves store the first half of its
             // runs, the others the second half.
             load_staged(prev, pbuf, j, ln, false);   // waited for by the first store
-            if (nb == 0) {   // no k-loop to carry the memory traffic
+            if (nb == 0)   // only in an image's last step (no row loads): no k-loop
                 for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
-                if (simd == DMA_SIMD)
-                    for (int r = 0; r < 2; ++r)
-                        for (int k = 0; k < ipr; ++k) stage_part(n, h0n + 2 * j + r, k, ln);
-            }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 if (bb >= nb) break;
-                const int pi = 32 * (simd + NSIMD * bb) + l32s;
-                const bool use = pi < npix;
-                const int pr = use ? div_w(pi, invW) : 0;
-                const int q = use ? pi - pr * W : 0;
+                const int px = 32 * (simd + NSIMD * bb) + l32s;   // pixel within the step
+                const bool use = px < npix;
+                const int pi = a + (use ? px : 0);
+                const int pr = div_w(pi, mW);
+                const int q = pi - pr * W;
                 BlockAddr ba;
 #pragma unroll
                 for (int r = 0; r < 3; ++r) {
-                    int sl = (p0 % NSLOT) + pr + r;        // slot of input row p0 + pr + r - 1
-                    if (sl >= NSLOT) sl -= NSLOT;
+                    int sl = fslot + (pr - ofr) + r;            // slot of input row pr + r - 1
                     if (sl >= NSLOT) sl -= NSLOT;
                     ba.rb[r] = (int)lbase + sl * SLOT + q * PXB;
                 }
 #pragma unroll
-                for (int sx = 0; sx < 3; ++sx) ba.cx[sx] = (his ^ perm(q + sx)) << 4;
+                for (int sx = 0; sx < 3; ++sx) {
+                    // rows pr - 1 and pr + 1 share a flip; row pr's differs when W / 8 is odd
+                    ba.cx[0][sx] = (his ^ perm(q + sx) ^ row_flip(pr - 1, ipr)) << 4;
+                    ba.cx[1][sx] = ba.cx[0][sx] ^ ((ipr & 1) << 6);
+                }
 
                 f32x16 acc;
-                if (memw && bb == 0) {
-                    // k-steps 2..5: the first half of the previous step's z runs (its LDS
-                    // reads have landed by then); 6..19 on SIMD 3: the row loads
+                if (bb == 0) {
+                    // k-steps 2..5: this wave's half of the previous step's z runs (its LDS
+                    // reads have landed by then); 6 .. 6 + LPW - 1: the row loads
                     auto side = [&](auto tc) {
                         constexpr int T = decltype(tc)::value;
                         // an opaque lane id per k-step keeps each instruction's address
@@ -409,23 +437,9 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                         int lt = ln;
                         asm volatile("" : "+v"(lt));
                         if constexpr (T >= 2 && T < 6) {
-                            store_staged(prev, 0, T - 2, lt);
-                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + 2 * DMA_MAX) {
-                            if (simd == DMA_SIMD) row_part(tc, lt);
-                        }
-                    };
-                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
-                } else if (bb == 0) {
-                    // k-steps 2..5: the second half of the previous step's z runs; 6..19 on
-                    // SIMD 3: the row loads
-                    auto side = [&](auto tc) {
-                        constexpr int T = decltype(tc)::value;
-                        int lt = ln;
-                        asm volatile("" : "+v"(lt));
-                        if constexpr (T >= 2 && T < 6) {
-                            store_staged(prev, 1, T - 2, ln);
-                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + 2 * DMA_MAX) {
-                            if (simd == DMA_SIMD) row_part(tc, lt);
+                            store_staged(prev, j, T - 2, lt);
+                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + LPW) {
+                            row_part(tc, lt);
                         }
                     };
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
@@ -434,19 +448,19 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 }
                 if (full)
-                    epilogue<false>(acc, use, stg, pi, j, his, s1, s2);
+                    epilogue<false>(acc, use, stg, px, j, his, s1, s2);
                 else
-                    epilogue<true>(acc, use, stg, pi, j, his, s1, s2);
+                    epilogue<true>(acc, use, stg, px, j, his, s1, s2);
             }
 
             // The staged rows must have landed before any wave reads them: wait for this
             // wave's loads, then the barrier publishes every wave's.  The barrier also
-            // frees the slots this step read for the step after next, and publishes this
+            // frees the slots this step read for the steps after it, and publishes this
             // step's staged z.
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             prev.nq = npix / 8;
-            prev.zr = make_rsrc(p.z + ((size_t)n * H + p0) * W * HK, npix * HK * 2);
+            prev.zr = make_rsrc(p.z + ((size_t)n * HW + a) * HK, npix * HK * 2);
             pbuf = cbuf;
         }
     }
@@ -485,27 +499,41 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
 
 }  // namespace
 
+// Ring slots: the input rows of a step and the rows the next one adds, ofr(s) - 1 ..
+// olr(s + 1) + 1, number at most floor((2 SP - 1) / W) + 4 (the output rows of 2 SP
+// consecutive pixels span at most floor((2 SP - 1) / W) + 2 rows).
+int halo_nslot(const ConvGeom &g) { return (2 * SP - 1) / g.W + 4; }
+
+// Input rows of an image's first step: -1 .. its last output row + 1.
+int halo_rows0(const ConvGeom &g) { return (std::min(SP, g.H * g.W) - 1) / g.W + 3; }
+
+size_t halo_lds_bytes(const ConvGeom &g)
+{
+    const size_t slot = (size_t)(g.W + 2) * PXB;
+    return std::max({halo_nslot(g) * slot + 2 * STG_BYTES, halo_rows0(g) * slot + FILTER_BYTES,
+                     (size_t)STATS_BYTES});
+}
+
 bool halo_eligible(const ConvGeom &g)
 {
-    return g.C == HC && g.K == HK && g.R == 3 && g.S == 3 && g.sh == 1 && g.sw == 1 && g.ph == 1 &&
-           g.pw == 1 && g.W >= 8 && g.W <= MAXW && g.W % 8 == 0 && g.P == g.H && g.Q == g.W;
+    if (!(g.C == HC && g.K == HK && g.R == 3 && g.S == 3 && g.sh == 1 && g.sw == 1 && g.ph == 1 && g.pw == 1 &&
+          g.W >= 8 && g.W <= MAXW && g.W % 8 == 0 && g.P == g.H && g.Q == g.W && g.H >= 1))
+        return false;
+    // pixel indices of an image (and of the step past its end) must stay below 2^32 / W
+    // for the multiply-high division, and in int range
+    const uint64_t hw = (uint64_t)g.H * g.W + SP;
+    return hw * g.W < (1ull << 32) && halo_lds_bytes(g) <= (size_t)HALO_MAX_LDS;
 }
 
 int halo_grid(const ConvGeom &g) { return std::min(g.N, HALO_MAX_GRID); }
 
-size_t halo_lds_bytes(const ConvGeom &g)
-{
-    const size_t ring = (size_t)NSLOT * (g.W + 2) * PXB;
-    return std::max({ring + 2 * STG_BYTES, (size_t)6 * (g.W + 2) * PXB + FILTER_BYTES, (size_t)STATS_BYTES});
-}
-
 hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
                                     float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    static_assert(NSLOT * (MAXW + 2) * PXB + 2 * STG_BYTES <= HALO_MAX_LDS && STATS_BYTES <= HALO_MAX_LDS &&
-                      6 * (MAXW + 2) * PXB + FILTER_BYTES <= HALO_MAX_LDS,
-                  "LDS bound");
-    HaloParams prm{x, w, z, partials, g.N, g.H, g.W, (g.W + 2) * PXB, (65536u + g.W - 1) / g.W};
+    static_assert(((2 * SP - 1) / MAXW + 4) * (MAXW + 2) * PXB + 2 * STG_BYTES <= HALO_MAX_LDS,
+                  "the ring for W = MAXW fits");
+    const uint32_t mW = (uint32_t)(((1ull << 32) + g.W - 1) / g.W);
+    HaloParams prm{x, w, z, partials, g.N, g.H, g.W, (g.W + 2) * PXB, halo_nslot(g), mW};
     const size_t lds = halo_lds_bytes(g);
     static bool attr_set = false;
     if (!attr_set) {

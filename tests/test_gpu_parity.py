@@ -42,18 +42,23 @@ def test_train_forward_small(g):
     H.check_train(g, d, res, ora)
 
 
-# The persistent 3x3 / 64-channel kernel (W a multiple of 8, 8..56): partial last steps,
-# several images per workgroup (N > 256), short and narrow images, partial pixel blocks.
+# The persistent 3x3 / 64-channel kernel (W a multiple of 8, 8..56; steps of 256 pixels
+# that start anywhere in a row): partial last steps and pixel blocks, steps spanning up
+# to 33 rows, several images per workgroup (N > 256), images smaller than one step.
 # The 64-channel 3x3 shapes it does not take (W % 8 != 0) run the generic conv.
 HALO_GEOMS = [
-    Geometry(2, 12, 16, 64, 64, 3, 3, 1, 1),     # three 4-row steps of 2 blocks
-    Geometry(3, 9, 24, 64, 64, 3, 3, 1, 1),      # 96-pixel steps, a one-row last step
-    Geometry(1, 56, 56, 64, 64, 3, 3, 1, 1),     # one full image, fourteen steps
+    Geometry(2, 12, 16, 64, 64, 3, 3, 1, 1),     # one step of 6 blocks
+    Geometry(3, 9, 24, 64, 64, 3, 3, 1, 1),      # one step of 6.75 blocks
+    Geometry(1, 56, 56, 64, 64, 3, 3, 1, 1),     # one full image, thirteen steps
     Geometry(300, 5, 8, 64, 64, 3, 3, 1, 1),     # two images for some workgroups
-    Geometry(2, 3, 56, 64, 64, 3, 3, 1, 1),      # fewer rows than a step
-    Geometry(2, 17, 8, 64, 64, 3, 3, 1, 1),      # the narrowest image: one block per step
-    Geometry(1, 6, 40, 64, 64, 3, 3, 1, 1),      # 5 blocks per step
-    Geometry(2, 7, 48, 64, 64, 3, 3, 1, 1),      # a 3-row last step of 4.5 blocks
+    Geometry(2, 3, 56, 64, 64, 3, 3, 1, 1),      # fewer pixels than a step
+    Geometry(2, 17, 8, 64, 64, 3, 3, 1, 1),      # the narrowest image
+    Geometry(1, 6, 40, 64, 64, 3, 3, 1, 1),      # 7.5 blocks
+    Geometry(2, 7, 48, 64, 64, 3, 3, 1, 1),      # a full step, then 2.5 blocks
+    Geometry(2, 29, 56, 64, 64, 3, 3, 1, 1),     # steps starting mid-row, a 1/3 last step
+    Geometry(1, 40, 24, 64, 64, 3, 3, 1, 1),     # 3.75 steps of up to 12 rows
+    Geometry(1, 70, 8, 64, 64, 3, 3, 1, 1),      # steps of 32 rows
+    Geometry(300, 9, 32, 64, 64, 3, 3, 1, 1),    # a step and a block per image, N > 256
     Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1),     # generic conv (W % 8 != 0)
     Geometry(300, 5, 7, 64, 64, 3, 3, 1, 1),     # generic conv, N > 256
 ]
