@@ -125,11 +125,11 @@ __device__ __forceinline__ void lds_wait(bf16x8 &x)
 
 // The 36 k-steps of one pixel block for the wave's 32 output channels: per k-step one
 // LDS fragment read and one MFMA, the filter fragment from registers.  Fragments are read
-// KD - 1 k-steps ahead.  side(integral_constant<T>) issues the memory instructions that
-// belong to k-step T.
+// KD - 2 k-steps ahead, each issued after the MFMA of the k-step before it.
+// side(integral_constant<T>) issues the memory instructions that belong to k-step T.
 template <typename Side>
 struct KLoop {
-    static constexpr int KD = 3;
+    static constexpr int KD = 4;
     const bf16x8 (&wf)[KSTEPS];
     const BlockAddr &ba;
     f32x16 &acc;
@@ -147,12 +147,18 @@ struct KLoop {
     template <int T>
     __device__ __forceinline__ void step()
     {
-        if constexpr (T + KD - 1 < KSTEPS) read<T + KD - 1>();
-        // the reads of k-steps T + 1 .. min(T + KD - 1, 35) may stay in flight
-        constexpr int newer = (KSTEPS - 1 - T) < (KD - 1) ? (KSTEPS - 1 - T) : (KD - 1);
+        // the reads of k-steps T + 1 .. min(T + KD - 2, 35) may stay in flight
+        constexpr int newer = (KSTEPS - 1 - T) < (KD - 2) ? (KSTEPS - 1 - T) : (KD - 2);
         lds_wait<newer>(xf[T % KD]);
         __builtin_amdgcn_sched_barrier(0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[T], xf[T % KD], T == 0 ? f32x16{} : acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // The read for k-step T + KD - 1 goes after MFMA T, into the fragment set of MFMA
+        // T - 1, which has finished (MFMA T depends on it).  MFMA T's own fragment is kept
+        // live past the read, so that neither the read nor its address arithmetic reuses
+        // registers the in-flight MFMA still reads (such a write waits for the MFMA).
+        if constexpr (T + KD - 1 < KSTEPS) read<T + KD - 1>();
+        asm volatile("" ::"v"(xf[T % KD]));
         side(std::integral_constant<int, T>{});
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (T + 1 < KSTEPS) step<T + 1>();
@@ -268,17 +274,23 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     };
     // A step's 1 KB z runs q = wave % 4 + 4 (4 half + k), k < 4, go out in two halves of
     // four: half 0 from the waves of channel half 0, half 1 from the others.
-    // load_staged reads a half of staging buffer buf into sd.
-    auto load_staged = [&](Staged &sd, int buf, int half, int ln, bool wait_now = true) {
-        const uint8_t *sb = stg0 + buf * STG_BYTES;
+    // load_staged reads a half of staging buffer buf into sd, with reads in assembly that
+    // the compiler does not track (its own waits for them, at the stores inside the first
+    // k-loop, would count only these four reads and drain the k-loop's read-ahead).  The
+    // k-loop's first wait (all but the two newest LDS operations done) covers them before
+    // its stores, LDS operations completing in order; elsewhere staged_wait precedes the
+    // stores.
+    auto load_staged = [&](Staged &sd, int buf, int half, int ln) {
+        const uint32_t sb = lbase + (uint32_t)(NSLOT * SLOT + buf * STG_BYTES);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int px = 8 * (simd + NSIMD * (4 * half + k)) + (ln >> 3);   // < SP
-            sd.d[k] = *(const u32x4 *)(sb + px * PXB + (((ln & 7) ^ perm(px)) << 4));
+            const uint32_t a = sb + px * PXB + (((ln & 7) ^ perm(px)) << 4);
+            asm volatile("ds_read_b128 %0, %1" : "=v"(sd.d[k]) : "v"(a) : "memory");
         }
-        // A use here makes the compiler wait for the reads now, not at the first store
-        // inside the k-loop, where its wait would also drain the k-loop's read-ahead.
-        if (wait_now) asm volatile("" ::"v"(sd.d[0]), "v"(sd.d[1]), "v"(sd.d[2]), "v"(sd.d[3]));
+    };
+    auto staged_wait = [](Staged &sd) {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sd.d[0]), "+v"(sd.d[1]), "+v"(sd.d[2]), "+v"(sd.d[3]));
     };
     // Runs q >= nq lie past the end of zr (npix * 128 = nq * 1024 bytes): the buffer
     // store drops them, so no condition is needed.  The stores stream (nt) and write
@@ -401,9 +413,11 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
             uint8_t *const stg = stg0 + cbuf * STG_BYTES;
             // The previous step's z: channel half 0's waves store the first half of its
             // runs, the others the second half.
-            load_staged(prev, pbuf, j, ln, false);   // waited for by the first store
-            if (nb == 0)   // only in an image's last step (no row loads): no k-loop
+            load_staged(prev, pbuf, j, ln);
+            if (nb == 0) {   // only in an image's last step (no row loads): no k-loop
+                staged_wait(prev);
                 for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
+            }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 if (bb >= nb) break;
@@ -465,6 +479,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
         }
     }
     load_staged(prev, pbuf, j, lane);
+    staged_wait(prev);
     for (int k = 0; k < 4; ++k) store_staged(prev, j, k, lane);
     __syncthreads();   // every wave is done with the staging buffers and the ring
 
