@@ -210,16 +210,13 @@ __device__ __forceinline__ void epilogue(const f32x16 &acc, bool use, uint8_t *s
 #pragma unroll
         for (int c = 0; c < 16; ++c) v[c] = use ? v[c] : 0.f;
     }
-    // squares first, then the swaps in place: no value is needed after its swap
-    float q[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) q[c] = v[c] * v[c];
+    // after the swap both values of pair i are the same channel: their sum goes to s1,
+    // their squares to s2 (two fused multiply-adds)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         swap_rows(v[i], v[i + 8]);
         s1[i] += v[i] + v[i + 8];
-        swap_rows(q[i], q[i + 8]);
-        s2[i] += q[i] + q[i + 8];
+        s2[i] = fmaf(v[i + 8], v[i + 8], fmaf(v[i], v[i], s2[i]));
     }
 }
 
