@@ -82,15 +82,16 @@ __global__ __launch_bounds__(NT) void bnbwd_reduce_kernel(const u32x4 *__restric
 // dbeta = s1, dgamma = s2 (fp64 over the partial rows, fixed order); coefficients of
 // the apply step: coef[0] = gamma*invstd, coef[1] = dbeta/M, coef[2] = dgamma/M.
 // Block b owns channels 4b..4b+3.
-__global__ __launch_bounds__(NT) void bnbwd_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
+template <int NTB>
+__global__ __launch_bounds__(NTB) void bnbwd_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
                                                             const float *__restrict__ gamma,
                                                             const float *__restrict__ invstd,
                                                             float *__restrict__ coef, float *__restrict__ dgamma,
                                                             float *__restrict__ dbeta)
 {
-    __shared__ double red[COLSUM_NT * 8];
+    __shared__ double red[NTB * 8];
     const int k0 = 4 * blockIdx.x;
-    colsum_pair4(rows, R, K, k0, red);
+    colsum_pair4<NTB>(rows, R, K, k0, red);
     if (threadIdx.x < 4) {
         const int k = k0 + threadIdx.x;
         const double s1 = red[threadIdx.x], s2 = red[4 + threadIdx.x];
@@ -179,8 +180,12 @@ hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *
     hipError_t e = launch(bnbwd_reduce_kernel, dim3(Bn), dim3(NT), 0, st, e0, nullptr, (const u32x4 *)dy, mask,
                           (const u32x4 *)z, saved_mean, saved_invstd, (int)M, K, rows, part);
     if (e != hipSuccess) return e;
-    e = launch(bnbwd_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, nullptr, nullptr, (const float *)part, Bn, K,
-               (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
+    if (Bn <= COLSUM_SMALL_R)
+        e = launch(bnbwd_finalize_kernel<COLSUM_NT_SMALL>, dim3(K / 4), dim3(COLSUM_NT_SMALL), 0, st, nullptr, nullptr,
+                   (const float *)part, Bn, K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
+    else
+        e = launch(bnbwd_finalize_kernel<COLSUM_NT_LARGE>, dim3(K / 4), dim3(COLSUM_NT_LARGE), 0, st, nullptr, nullptr,
+                   (const float *)part, Bn, K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
     if (e != hipSuccess) return e;
     const int chunks = (int)(M * K / 8);
     const int cpr = K / 8;

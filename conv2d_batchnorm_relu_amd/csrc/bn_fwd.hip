@@ -9,12 +9,13 @@ constexpr int NT = 256;
 
 // The BN finalize (bn_finalize_channel) over the R partial rows ([R][2][K], sums then
 // sums of squares).  Block b owns channels 4b..4b+3.
-__global__ __launch_bounds__(NT) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K,
+template <int NTB>
+__global__ __launch_bounds__(NTB) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K,
                                                             BnFinalizeArgs f)
 {
-    __shared__ double red[COLSUM_NT * 8];
+    __shared__ double red[NTB * 8];
     const int k0 = 4 * blockIdx.x;
-    colsum_pair4(rows, R, K, k0, red);
+    colsum_pair4<NTB>(rows, R, K, k0, red);
     if (threadIdx.x < 4) bn_finalize_channel(f, k0 + threadIdx.x, red[threadIdx.x], red[4 + threadIdx.x]);
 }
 
@@ -115,7 +116,11 @@ int train_partial_rows(const ConvGeom &g)
 hipError_t launch_stats_finalize(int rows, int K, const float *partials, const BnFinalizeArgs &fin, hipStream_t st,
                                  hipEvent_t e0, hipEvent_t e1)
 {
-    return launch(stats_finalize_kernel, dim3(K / 4), dim3(NT), 0, st, e0, e1, partials, rows, K, fin);
+    if (rows <= COLSUM_SMALL_R)
+        return launch(stats_finalize_kernel<COLSUM_NT_SMALL>, dim3(K / 4), dim3(COLSUM_NT_SMALL), 0, st, e0, e1, partials,
+                      rows, K, fin);
+    return launch(stats_finalize_kernel<COLSUM_NT_LARGE>, dim3(K / 4), dim3(COLSUM_NT_LARGE), 0, st, e0, e1, partials,
+                  rows, K, fin);
 }
 
 hipError_t launch_bn_apply_relu_mask(long M, int K, const uint16_t *z, const float *scale,

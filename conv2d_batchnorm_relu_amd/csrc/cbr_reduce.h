@@ -7,13 +7,16 @@
 
 namespace cbr {
 
-constexpr int COLSUM_NT = 256;   // threads per block of the column-sum kernels
+// Threads per block of the column-sum kernels: one wave for up to COLSUM_SMALL_R rows
+// (fewer tree levels and barriers), four waves for more rows.
+constexpr int COLSUM_NT_SMALL = 64, COLSUM_NT_LARGE = 256, COLSUM_SMALL_R = 1024;
 
-// Called by all COLSUM_NT threads of a block that owns channels k0..k0+3 (k0 % 4 == 0).
-// Thread t sums rows t, t + 256, ... of columns k0..k0+3 and K+k0..K+k0+3 (eight 16-byte
+// Called by all NTB threads of a block that owns channels k0..k0+3 (k0 % 4 == 0).
+// Thread t sums rows t, t + NTB, ... of columns k0..k0+3 and K+k0..K+k0+3 (eight 16-byte
 // loads in flight at a time), then a fixed halving tree over the threads combines them.
-// red (LDS) holds COLSUM_NT * 8 doubles; on return red[e] (e < 4) is the sum of column
+// red (LDS) holds NTB * 8 doubles; on return red[e] (e < 4) is the sum of column
 // k0 + e and red[4 + e] that of column K + k0 + e, visible to every thread.
+template <int NTB>
 __device__ inline void colsum_pair4(const float *__restrict__ rows, int R, int K, int k0, double *red)
 {
     constexpr int UN = 8;
@@ -21,11 +24,11 @@ __device__ inline void colsum_pair4(const float *__restrict__ rows, int R, int K
     double a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = 0.0;
-    for (int r0 = tid; r0 < R; r0 += COLSUM_NT * UN) {
+    for (int r0 = tid; r0 < R; r0 += NTB * UN) {
         f32x4 v[UN][2];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int r = r0 + u * COLSUM_NT;
+            const int r = r0 + u * NTB;
             if (r < R) {
                 const float *row = rows + (size_t)r * 2 * K;
                 v[u][0] = *(const f32x4 *)(row + k0);
@@ -46,7 +49,7 @@ __device__ inline void colsum_pair4(const float *__restrict__ rows, int R, int K
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[tid * 8 + e] = a[e];
     __syncthreads();
-    for (int s = COLSUM_NT / 2; s > 0; s >>= 1) {
+    for (int s = NTB / 2; s > 0; s >>= 1) {
         if (tid < s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) red[tid * 8 + e] += red[(tid + s) * 8 + e];
