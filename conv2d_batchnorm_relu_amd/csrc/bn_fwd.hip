@@ -89,17 +89,16 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
                                                      float eps, int K, int Kg, uint16_t *__restrict__ wf,
                                                      float *__restrict__ bf)
 {
-    const long total = (long)K * Kg;
-    for (long i = (long)blockIdx.x * NT + threadIdx.x; i < total; i += (long)gridDim.x * NT) {
-        const int k = (int)(i / Kg);
-        const double sd = (double)gamma[k] / sqrt((double)rv[k] + (double)eps);
-        wf[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(w[i]) * (float)sd);
-        if (i < K) {
-            const int kb = (int)i;
-            const double s2 = (double)gamma[kb] / sqrt((double)rv[kb] + (double)eps);
-            const double b = bias ? (double)bias[kb] : 0.0;
-            bf[kb] = (float)((b - (double)rm[kb]) * s2 + (double)beta[kb]);
-        }
+    // block k folds output channel k: s_k once, then its Kg filter values
+    const int k = blockIdx.x;
+    const double sd = (double)gamma[k] / sqrt((double)rv[k] + (double)eps);
+    const float sf = (float)sd;
+    const uint16_t *wk = w + (size_t)k * Kg;
+    uint16_t *wfk = wf + (size_t)k * Kg;
+    for (int i = threadIdx.x; i < Kg; i += NT) wfk[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(wk[i]) * sf);
+    if (threadIdx.x == 0) {
+        const double b = bias ? (double)bias[k] : 0.0;
+        bf[k] = (float)((b - (double)rm[k]) * sd + (double)beta[k]);
     }
 }
 
@@ -141,10 +140,8 @@ hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, c
                           const float *beta, const float *rm, const float *rv, float eps,
                           uint16_t *w_fold, float *b_fold, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const long total = (long)K * Kg;
-    const int blocks = (int)std::min<long>((total + NT - 1) / NT, 4096);
-    return launch(bn_fold_kernel, dim3(blocks), dim3(NT), 0, st, e0, e1, w, bias, gamma, beta, rm, rv, eps, K, Kg,
-                  w_fold, b_fold);
+    return launch(bn_fold_kernel, dim3(K), dim3(NT), 0, st, e0, e1, w, bias, gamma, beta, rm, rv, eps, K, Kg, w_fold,
+                  b_fold);
 }
 
 }  // namespace cbr
