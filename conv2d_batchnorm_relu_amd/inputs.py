@@ -31,16 +31,34 @@ class Geometry:
     k: int
     r: int
     s: int
-    stride: int = 1
-    pad: int = 1
+    stride: int = 1               # vertical stride (both axes unless stride_w is given)
+    pad: int = 1                  # vertical zero padding (both axes unless pad_w is given)
+    stride_w: int | None = None   # horizontal stride when it differs from the vertical one
+    pad_w: int | None = None      # horizontal padding when it differs from the vertical one
+
+    @property
+    def sh(self) -> int:
+        return self.stride
+
+    @property
+    def sw(self) -> int:
+        return self.stride if self.stride_w is None else self.stride_w
+
+    @property
+    def ph(self) -> int:
+        return self.pad
+
+    @property
+    def pw(self) -> int:
+        return self.pad if self.pad_w is None else self.pad_w
 
     @property
     def p(self) -> int:
-        return (self.h + 2 * self.pad - self.r) // self.stride + 1
+        return (self.h + 2 * self.ph - self.r) // self.sh + 1
 
     @property
     def q(self) -> int:
-        return (self.w + 2 * self.pad - self.s) // self.stride + 1
+        return (self.w + 2 * self.pw - self.s) // self.sw + 1
 
     @property
     def m(self) -> int:

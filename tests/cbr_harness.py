@@ -33,12 +33,12 @@ def log(msg):
 
 
 def oshape(g: Geometry):
-    return oracle.OShape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.stride, g.pad, g.pad)
+    return oracle.OShape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.sh, g.sw, g.ph, g.pw)
 
 
 def cshape(g: Geometry):
     import conv2d_batchnorm_relu_amd as cbr
-    return cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.pad)
+    return cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.sh, g.ph, stride_w=g.sw, pad_w=g.pw)
 
 
 def dev_bf16(a, device="cuda"):

@@ -18,7 +18,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def oshape(g: Geometry) -> OShape:
-    return OShape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.stride, g.pad, g.pad)
+    return OShape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.sh, g.sw, g.ph, g.pw)
 
 
 def brute_conv(x, w, sh, sw, ph, pw):
@@ -47,7 +47,14 @@ GEOMS = [
     Geometry(2, 5, 6, 5, 3, 1, 1, 1, 0),      # 1x1
     Geometry(1, 7, 6, 2, 3, 3, 3, 2, 0),      # stride 2, no padding, ragged
     Geometry(1, 4, 4, 3, 2, 3, 3, 1, 2),      # padding wider than the filter reach
+] + [
+    # Anisotropic geometry: every axis pair differs (stride, padding, filter size, image
+    # size), so an index that reads the other axis's stride or padding fails.
+    Geometry(2, 9, 7, 3, 4, 3, 5, stride=2, pad=1, stride_w=1, pad_w=2),    # stride (2,1), pad (1,2), 3x5
+    Geometry(1, 11, 6, 2, 3, 7, 1, stride=1, pad=3, stride_w=2, pad_w=0),   # 7x1, stride (1,2), pad (3,0)
+    Geometry(1, 8, 10, 3, 2, 1, 3, stride=3, pad=0, stride_w=1, pad_w=1),   # 1x3, stride (3,1), pad (0,1)
 ]
+ANISO = GEOMS[-3:]
 
 
 @pytest.mark.parametrize("g", GEOMS, ids=str)
@@ -56,7 +63,7 @@ def test_conv_matches_brute_force(g):
     x = rng.standard_normal((g.n, g.h, g.w, g.c))
     w = rng.standard_normal((g.k, g.r, g.s, g.c))
     z = oracle.conv2d(oshape(g), x, w)
-    ref = brute_conv(x, w, g.stride, g.stride, g.pad, g.pad)
+    ref = brute_conv(x, w, g.sh, g.sw, g.ph, g.pw)
     assert z.shape == ref.shape == (g.n, g.p, g.q, g.k)
     np.testing.assert_allclose(z, ref, rtol=1e-13, atol=1e-13)
 
@@ -69,7 +76,7 @@ def test_conv_matches_torch_conv2d(g):
     b = rng.standard_normal(g.k)
     z = oracle.conv2d(oshape(g), x, w, b)
     zt = F.conv2d(torch.from_numpy(x).permute(0, 3, 1, 2), torch.from_numpy(w).permute(0, 3, 1, 2),
-                  torch.from_numpy(b), stride=g.stride, padding=g.pad).permute(0, 2, 3, 1).numpy()
+                  torch.from_numpy(b), stride=(g.sh, g.sw), padding=(g.ph, g.pw)).permute(0, 2, 3, 1).numpy()
     np.testing.assert_allclose(z, zt, rtol=1e-12, atol=1e-12)
 
 
@@ -93,8 +100,8 @@ def test_conv_centre_delta_is_identity():
     np.testing.assert_array_equal(oracle.conv2d(oshape(g), x, w), x)
 
 
-def test_conv_at_matches_full():
-    g = Geometry(2, 9, 7, 5, 6, 3, 3, 2, 1)
+@pytest.mark.parametrize("g", [Geometry(2, 9, 7, 5, 6, 3, 3, 2, 1)] + ANISO, ids=str)
+def test_conv_at_matches_full(g):
     rng = np.random.default_rng(15)
     x = rng.standard_normal((g.n, g.h, g.w, g.c))
     w = rng.standard_normal((g.k, g.r, g.s, g.c))
@@ -277,7 +284,8 @@ def test_bn_backward_invariants():
 
 
 @pytest.mark.parametrize("g", [Geometry(2, 8, 8, 4, 8, 3, 3, 1, 1), Geometry(2, 9, 11, 3, 5, 7, 7, 2, 3),
-                               Geometry(1, 7, 6, 6, 4, 3, 3, 2, 0), Geometry(2, 5, 5, 3, 2, 1, 1, 1, 0)], ids=str)
+                               Geometry(1, 7, 6, 6, 4, 3, 3, 2, 0), Geometry(2, 5, 5, 3, 2, 1, 1, 1, 0)] + ANISO,
+                         ids=str)
 def test_dgrad_wgrad_adjointness(g):
     """<conv(x,w), dz> = <x, dgrad(dz,w)> = <w, wgrad(dz,x)> for an independent random dz."""
     rng = np.random.default_rng(16)
@@ -292,15 +300,15 @@ def test_dgrad_wgrad_adjointness(g):
     assert abs(a - c) <= 1e-11 * (1 + abs(a))
 
 
-def test_dgrad_wgrad_match_torch():
-    g = Geometry(2, 9, 11, 3, 5, 7, 7, 2, 3)
+@pytest.mark.parametrize("g", [Geometry(2, 9, 11, 3, 5, 7, 7, 2, 3)] + ANISO, ids=str)
+def test_dgrad_wgrad_match_torch(g):
     rng = np.random.default_rng(17)
     x = torch.from_numpy(rng.standard_normal((g.n, g.h, g.w, g.c)))
     w = torch.from_numpy(rng.standard_normal((g.k, g.r, g.s, g.c)))
     dz = torch.from_numpy(rng.standard_normal((g.n, g.p, g.q, g.k)))
     xt = x.permute(0, 3, 1, 2).clone().requires_grad_()
     wt = w.permute(0, 3, 1, 2).clone().requires_grad_()
-    (F.conv2d(xt, wt, stride=g.stride, padding=g.pad) * dz.permute(0, 3, 1, 2)).sum().backward()
+    (F.conv2d(xt, wt, stride=(g.sh, g.sw), padding=(g.ph, g.pw)) * dz.permute(0, 3, 1, 2)).sum().backward()
     sp = oshape(g)
     np.testing.assert_allclose(oracle.conv2d_dgrad(sp, dz.numpy(), w.numpy()),
                                xt.grad.permute(0, 2, 3, 1).numpy(), rtol=1e-12, atol=1e-12)
