@@ -31,9 +31,10 @@ class CbrShape(ctypes.Structure):
 
 
 class CbrError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: str | None = None):
         self.status = status
-        super().__init__(f"{where}: {cbr_status_str(status)} (status {status})")
+        msg = detail if detail is not None else cbr_status_str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
 
 
 _lib = None
@@ -87,18 +88,34 @@ def _sp(shape):
     return ctypes.byref(shape)
 
 
-def _ptr(t):
+_E_VALUE = 7   # CBR_E_VALUE: the binding reports unusable tensors with it
+
+
+def _ptr(t, itemsize, name, where):
+    """Device address of tensor t, after checking that the library can read it as the
+    dense array of itemsize-byte elements that include/cbr.h describes: a CUDA (HIP)
+    tensor, contiguous in its own layout, with that element size.  An integer is taken
+    as a raw device address; None stays NULL."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise CbrError(_E_VALUE, where, f"{name} is not a GPU tensor")
+    if not t.is_contiguous():
+        raise CbrError(_E_VALUE, where, f"{name} is not contiguous (the library reads dense NHWC/KRSC arrays)")
+    if t.element_size() != itemsize:
+        raise CbrError(_E_VALUE, where, f"{name} has {t.element_size()}-byte elements, expected {itemsize}")
     return t.data_ptr()
 
 
-def _ws(workspace):
+def _ws(workspace, where):
     if workspace is None:
         return None, 0
-    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if isinstance(workspace, tuple):
+        return workspace
+    p = _ptr(workspace, workspace.element_size(), "workspace", where)
+    return p, workspace.numel() * workspace.element_size()
 
 
 def _stream(stream):
@@ -144,34 +161,43 @@ def _events(events):
 def cbr_forward_train(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, momentum,
                       z, y, relu_mask, saved_mean, saved_invstd, run_mean_out, run_var_out,
                       workspace, stream=None, events=None):
-    ws, nbytes = _ws(workspace)
-    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(gamma), _ptr(beta), _ptr(run_mean_in), _ptr(run_var_in),
-            float(eps), float(momentum), _ptr(z), _ptr(y), _ptr(relu_mask), _ptr(saved_mean),
-            _ptr(saved_invstd), _ptr(run_mean_out), _ptr(run_var_out), ws, nbytes, _stream(stream))
+    f = "cbr_forward_train"
+    ws, nbytes = _ws(workspace, f)
+    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(gamma, 4, "gamma", f),
+            _ptr(beta, 4, "beta", f), _ptr(run_mean_in, 4, "run_mean_in", f), _ptr(run_var_in, 4, "run_var_in", f),
+            float(eps), float(momentum), _ptr(z, 2, "z", f), _ptr(y, 2, "y", f), _ptr(relu_mask, 4, "relu_mask", f),
+            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f),
+            _ptr(run_mean_out, 4, "run_mean_out", f), _ptr(run_var_out, 4, "run_var_out", f), ws, nbytes,
+            _stream(stream))
     if events is None:
-        _check(_load().cbr_forward_train(*args), "cbr_forward_train")
+        _check(_load().cbr_forward_train(*args), f)
     else:
         _check(_load().cbr_forward_train_ev(*args, _events(events)), "cbr_forward_train_ev")
 
 
 def cbr_forward_infer(shape, x, w, conv_bias, gamma, beta, run_mean, run_var, eps, y,
                       workspace, stream=None, events=None):
-    ws, nbytes = _ws(workspace)
-    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(conv_bias), _ptr(gamma), _ptr(beta), _ptr(run_mean),
-            _ptr(run_var), float(eps), _ptr(y), ws, nbytes, _stream(stream))
+    f = "cbr_forward_infer"
+    ws, nbytes = _ws(workspace, f)
+    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(conv_bias, 4, "conv_bias", f),
+            _ptr(gamma, 4, "gamma", f), _ptr(beta, 4, "beta", f), _ptr(run_mean, 4, "run_mean", f),
+            _ptr(run_var, 4, "run_var", f), float(eps), _ptr(y, 2, "y", f), ws, nbytes, _stream(stream))
     if events is None:
-        _check(_load().cbr_forward_infer(*args), "cbr_forward_infer")
+        _check(_load().cbr_forward_infer(*args), f)
     else:
         _check(_load().cbr_forward_infer_ev(*args, _events(events)), "cbr_forward_infer_ev")
 
 
 def cbr_backward(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd,
                  dz, dgamma, dbeta, dw, dx, workspace, stream=None, events=None):
-    ws, nbytes = _ws(workspace)
-    args = (_sp(shape), _ptr(x), _ptr(w), _ptr(z), _ptr(relu_mask), _ptr(dy), _ptr(gamma),
-            _ptr(saved_mean), _ptr(saved_invstd), _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(dw),
-            _ptr(dx), ws, nbytes, _stream(stream))
+    f = "cbr_backward"
+    ws, nbytes = _ws(workspace, f)
+    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(z, 2, "z", f),
+            _ptr(relu_mask, 4, "relu_mask", f), _ptr(dy, 2, "dy", f), _ptr(gamma, 4, "gamma", f),
+            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f), _ptr(dz, 2, "dz", f),
+            _ptr(dgamma, 4, "dgamma", f), _ptr(dbeta, 4, "dbeta", f), _ptr(dw, 4, "dw", f), _ptr(dx, 2, "dx", f),
+            ws, nbytes, _stream(stream))
     if events is None:
-        _check(_load().cbr_backward(*args), "cbr_backward")
+        _check(_load().cbr_backward(*args), f)
     else:
         _check(_load().cbr_backward_ev(*args, _events(events)), "cbr_backward_ev")

@@ -164,3 +164,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(cbr, "_lib", None)
     with pytest.raises(ImportError):
         cbr.cbr_status_str(0)
+
+
+def test_binding_rejects_unusable_tensors():
+    """The binding refuses host tensors, non-contiguous views and wrong element sizes
+    before anything reaches the library (it never reinterprets memory)."""
+    import torch
+    import conv2d_batchnorm_relu_amd as cbr
+    sp = cbr.make_shape(1, 4, 4, 8, 8, 3, 3, 1, 1)
+    host = torch.zeros(16, dtype=torch.bfloat16)
+    args = [host] * 6 + [1e-5, 0.1] + [host] * 8 + [None]
+    with pytest.raises(cbr.CbrError, match="not a GPU tensor"):
+        cbr.cbr_forward_train(sp, *args)
+    with pytest.raises(cbr.CbrError, match="not a GPU tensor"):
+        cbr.cbr_forward_infer(sp, host, host, None, host, host, host, host, 1e-5, host, None)
+    with pytest.raises(cbr.CbrError, match="not a GPU tensor"):
+        cbr.cbr_backward(sp, host, host, host, host, host, host, host, host, None, host, host, host, None, None)

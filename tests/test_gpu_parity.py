@@ -179,6 +179,98 @@ def test_backward_small(g, want_dx):
         assert bw["dx"] is None
 
 
+# Anisotropic geometry (stride, padding and filter size differ between the axes) through
+# every kernel family that accepts it: the generic conv, the large-tile conv, the
+# first-layer conv, both weight-gradient kernels and the data gradient.
+ANISO_TRAIN_GEOMS = [
+    Geometry(3, 9, 11, 16, 24, 3, 5, stride=2, pad=1, stride_w=1, pad_w=2),    # generic conv
+    Geometry(2, 13, 10, 8, 16, 7, 1, stride=1, pad=3, stride_w=2, pad_w=0),    # generic conv, 7x1
+    Geometry(3, 13, 11, 64, 256, 3, 5, stride=2, pad=1, stride_w=1, pad_w=2),  # large-tile conv
+    Geometry(2, 11, 15, 32, 128, 1, 3, stride=1, pad=0, stride_w=2, pad_w=1),  # large-tile conv, 1x3
+    Geometry(2, 32, 32, 3, 64, 7, 5, stride=2, pad=2, pad_w=1),                # first layer, 7x5
+    Geometry(2, 30, 24, 3, 64, 5, 7, stride=2, pad=1, pad_w=3),                # first layer, 5x7
+]
+ANISO_INFER_GEOMS = ANISO_TRAIN_GEOMS[:4] + [
+    Geometry(2, 19, 23, 32, 128, 7, 1, stride=1, pad=3, stride_w=2, pad_w=0),  # large-tile conv, 7x1
+]
+ANISO_BWD_GEOMS = [
+    (Geometry(2, 9, 11, 16, 24, 3, 5, stride=1, pad=1, pad_w=2), True),        # generic wgrad + dgrad
+    (Geometry(2, 10, 12, 128, 256, 3, 1, stride=1, pad=1, pad_w=0), True),     # transposed-read wgrad, large-tile dgrad
+    (Geometry(2, 13, 9, 128, 256, 3, 3, stride=2, pad=1, stride_w=1), False),  # transposed-read wgrad, stride (2,1)
+    (Geometry(3, 12, 10, 16, 32, 1, 3, stride=1, pad=0, stride_w=2, pad_w=1), False),  # generic wgrad, stride (1,2)
+    (Geometry(2, 31, 29, 3, 64, 7, 5, stride=2, pad=3, pad_w=1), False),       # first-layer wgrad, 7x5
+]
+
+
+@pytest.mark.parametrize("g", ANISO_TRAIN_GEOMS, ids=str)
+def test_train_forward_anisotropic(g):
+    H.log(f"train fwd (anisotropic) {g}")
+    d = draw(g, "train", 19)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    H.check_train(g, d, res, ora)
+
+
+@pytest.mark.parametrize("g", ANISO_INFER_GEOMS, ids=str)
+def test_infer_anisotropic(g):
+    H.log(f"infer (anisotropic) {g}")
+    d = draw(g, "infer", 20)
+    y = H.gpu_infer(g, d)
+    ref = H.oracle.forward_infer(H.oshape(g), d["x"], d["w"], d["bias"], d["gamma"], d["beta"],
+                                 d["run_mean"], d["run_var"], 1e-5)
+    H.assert_close(y, ref, "infer y")
+
+
+@pytest.mark.parametrize("g,want_dx", ANISO_BWD_GEOMS, ids=str)
+def test_backward_anisotropic(g, want_dx):
+    H.log(f"backward (anisotropic) {g} dx={want_dx}")
+    d = draw(g, "bwd", 21)
+    res, devt = H.gpu_train(g, d)
+    bw = H.gpu_backward(g, devt, d["dy"], want_dx=want_dx)
+    ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"], want_dx=want_dx)
+    H.check_backward(g, d, bw, ob, want_dx)
+
+
+# Channels whose batch mean is many standard deviations from zero: input channel 0 is the
+# constant 1 and the centre tap of each filter scales it, so every output pixel sees it
+# (the centre tap is never in the padding) and output channel k gets mean ~ +-ratio*sigma_k,
+# sigma_k the spread the other channels give it.  One geometry per statistics kernel.
+LARGE_MEAN_GEOMS = [
+    Geometry(2, 12, 16, 64, 64, 3, 3, 1, 1),       # persistent 3x3 conv
+    Geometry(3, 13, 11, 64, 256, 3, 3, 1, 1),      # large-tile conv
+    Geometry(3, 9, 11, 16, 24, 3, 3, 1, 1),        # generic conv
+    Geometry(2, 32, 32, 3, 64, 7, 7, 2, 3),        # first-layer conv
+]
+
+
+def large_mean_inputs(g, ratio, seed):
+    from conv2d_batchnorm_relu_amd.inputs import bf16_round
+    d = draw(g, "train", seed)
+    x = d["x"].copy()
+    x[..., 0] = 1.0
+    w = d["w"].copy()
+    w[:, g.r // 2, g.s // 2, 0] = 0.0
+    sigma = np.sqrt((w.astype(np.float64) ** 2).reshape(g.k, -1).sum(1))
+    sign = np.where(np.arange(g.k) % 2 == 0, 1.0, -1.0)
+    w[:, g.r // 2, g.s // 2, 0] = (sign * ratio * sigma).astype(np.float32)
+    d["x"], d["w"] = bf16_round(x), bf16_round(w)
+    return d
+
+
+@pytest.mark.parametrize("ratio", [10.0, 100.0])
+@pytest.mark.parametrize("g", LARGE_MEAN_GEOMS, ids=str)
+def test_train_forward_large_channel_mean(g, ratio):
+    H.log(f"train fwd (|mean|/sigma ~ {ratio}) {g}")
+    d = large_mean_inputs(g, ratio, 22)
+    res, _ = H.gpu_train(g, d)
+    ora = H.oracle_train(g, d)
+    got = np.abs(ora["mean"]) / np.sqrt(ora["var"])
+    assert got.min() > 0.5 * ratio, got.min()
+    # y and the mask are compared with the normalisation of the stored bf16 z: at these
+    # ratios the rounding of z to bf16 alone moves u by up to ratio * 2^-9 * gamma.
+    H.check_train(g, d, res, ora, y_from_stored_z=True)
+
+
 def test_backward_dz_in_workspace_and_dx_aliasing_x():
     """dz = NULL keeps dz in the workspace; dx may overwrite x in place."""
     g = Geometry(2, 12, 12, 32, 32, 3, 3, 1, 1)
@@ -252,7 +344,10 @@ def test_backward_full_workload():
     H.log(f"full backward {g}")
     res, devt = H.gpu_train(g, d, wl.eps, wl.momentum)
     bw = H.gpu_backward(g, devt, d["dy"])
-    H.log("oracle")
+    H.log("oracle forward")
+    ora = H.oracle_train(g, d, wl.eps, wl.momentum)
+    flips = H.check_train(g, d, res, ora, wl.eps, wl.momentum)
+    H.log(f"forward ok, mask flips near zero: {flips}; oracle backward")
     ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"])
     H.check_backward(g, d, bw, ob)
 
