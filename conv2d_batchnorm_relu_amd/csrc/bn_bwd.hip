@@ -89,12 +89,14 @@ __global__ __launch_bounds__(NTB) void bnbwd_finalize_kernel(const float *__rest
                                                             float *__restrict__ coef, float *__restrict__ dgamma,
                                                             float *__restrict__ dbeta)
 {
-    __shared__ double red[NTB * 8];
+    __shared__ double red[8 * NTB / 64];
     const int k0 = 4 * blockIdx.x;
-    colsum_pair4<NTB>(rows, R, K, k0, red);
+    double s[8];
+    colsum_pair4<NTB>(rows, R, K, k0, s, red);
     if (threadIdx.x < 4) {
-        const int k = k0 + threadIdx.x;
-        const double s1 = red[threadIdx.x], s2 = red[4 + threadIdx.x];
+        const int e = threadIdx.x, k = k0 + e;
+        const double s1 = e == 0 ? s[0] : e == 1 ? s[1] : e == 2 ? s[2] : s[3];
+        const double s2 = e == 0 ? s[4] : e == 1 ? s[5] : e == 2 ? s[6] : s[7];
         dbeta[k] = (float)s1;
         dgamma[k] = (float)s2;
         coef[k] = gamma[k] * invstd[k];

@@ -7,16 +7,23 @@ namespace {
 
 constexpr int NT = 256;
 
-// The BN finalize (bn_finalize_channel) over the R partial rows ([R][2][K], sums then
-// sums of squares).  Block b owns channels 4b..4b+3.
+// The BN finalize (bn_finalize_channel) over the R partial rows ([R][2][K] per-row means
+// and M2, then the [R] row counts).  Block b owns channels 4b..4b+3.
 template <int NTB>
 __global__ __launch_bounds__(NTB) void stats_finalize_kernel(const float *__restrict__ rows, int R, int K,
                                                             BnFinalizeArgs f)
 {
-    __shared__ double red[NTB * 8];
+    __shared__ double red[8 * NTB / 64];
     const int k0 = 4 * blockIdx.x;
-    colsum_pair4<NTB>(rows, R, K, k0, red);
-    if (threadIdx.x < 4) bn_finalize_channel(f, k0 + threadIdx.x, red[threadIdx.x], red[4 + threadIdx.x]);
+    double mean[4], m2[4];
+    chan_combine4<NTB>(rows, rows + (size_t)R * 2 * K, R, K, f.M, k0, mean, m2, red);
+    if (threadIdx.x < 4) {
+        // thread e finalizes channel k0 + e (constant indices: the arrays stay in registers)
+        const int e = threadIdx.x;
+        const double me = e == 0 ? mean[0] : e == 1 ? mean[1] : e == 2 ? mean[2] : mean[3];
+        const double qe = e == 0 ? m2[0] : e == 1 ? m2[1] : e == 2 ? m2[2] : m2[3];
+        bn_finalize_channel(f, k0 + e, me, qe);
+    }
 }
 
 // Normalise + ReLU + mask (CBR page, section 4.3): u = z*eq_scale + eq_bias, y = max(u, 0),

@@ -63,7 +63,7 @@ TrainLayout train_layout(const ConvGeom &g)
 {
     TrainLayout L;
     size_t o = 0;
-    L.partials = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)train_partial_rows(g));
+    L.partials = o; o = align_up(o + sizeof(float) * (2 * g.K + 1) * (size_t)train_partial_rows(g));
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
     L.wexp = o; o = align_up(o + (c3s2_eligible(g) ? c3s2_wexp_bytes(g) : 0));

@@ -68,7 +68,10 @@ size_t c3s2_wexp_bytes(const ConvGeom &g);
 hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *wexp,
                                   uint16_t *z, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 
-// Rows of per-channel partial sums the training forward produces (one [2][K] row each).
+// Rows of per-channel partial statistics the training forward produces.  The partials
+// area holds R rows of [2][K] fp32 (each channel's mean over the row's output pixels,
+// then its M2 = sum of squared deviations from that mean), followed by R fp32 pixel
+// counts; a row with count 0 holds zeros.
 int train_partial_rows(const ConvGeom &g);
 
 // Blocks of the BN-backward reduction over M rows of K channels.

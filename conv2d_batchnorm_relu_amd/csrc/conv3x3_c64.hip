@@ -32,7 +32,10 @@
 // holding 4 consecutive output channels of one pixel.  The waves on SIMD s take blocks
 // s and s + 4 of a step.
 // The statistics are accumulated per lane in fp32 registers across the whole persistent
-// loop and reduced across lanes and waves once at the end: one partial per workgroup.
+// loop, as sums of deviations (and their squares) from a per-lane shift -- the lane's own
+// first value of each channel, so the sums do not cancel when a channel's mean is far
+// from zero -- and combined across lanes and waves once at the end into one row of
+// (count, mean, M2) per workgroup.
 #include <hip/hip_ext.h>
 
 #include "cbr_launch.h"
@@ -50,7 +53,7 @@ constexpr int NSIMD = 4;
 constexpr int MAXW = 56;
 constexpr int KSTEPS = 36;              // 9 taps x 4 chunks of 16 input channels
 constexpr int STG_BYTES = SP * PXB;     // one step's z, pixel-major
-constexpr int STATS_BYTES = 16 * NT * 4;     // final cross-lane reduction area
+constexpr int STATS_BYTES = NW * 4 * 17 * 4;    // final cross-lane combination area
 constexpr int FILTER_BYTES = HK * 72 * 16;    // the filter, staged once through LDS
 // Row loads per wave per step: a step adds at most ceil(SP / W) input rows of W / 8
 // loads each, i.e. at most SP / 8 + W / 8 <= 39 loads over the 8 waves.
@@ -191,33 +194,52 @@ __device__ __forceinline__ void swap_rows(float &a, float &b)
 
 // Statistics and staging of one pixel block.  The lane holds, for pixel l32 of the
 // block, channels 32j + 8g + 4hi + e in acc[4g + e] (32x32x16 layout: row
-// 8*(v/4) + 4*(l/32) + v%4).  Running sums s1[i], s2[i] (i = 4g + e, g < 2) of lane l
-// cover channel 32j + 8(g + 2 ((l / 16) % 2)) + 4hi + e over pixel pairs (l, l ^ 16);
-// with MASKED, lanes of pixels past the step (!use) add zeros.  The bf16 results go to
-// staging row px (16-byte chunk c of a row at position c ^ perm(px)).
+// 8*(v/4) + 4*(l/32) + v%4).  After the swap, pair i (i = 4g + e, g < 2) of lane l holds
+// channel 32j + 8(g + 2 ((l / 16) % 2)) + 4hi + e of pixels l and l ^ 16 (in that order
+// in even 16-lane rows, the other way round in odd ones).  Running sums s1[i], s2[i] are
+// of the deviations d = z - c[i] from the lane's shift c[i], which the wave's first
+// block sets to the pair's first value (the shifted-data form of the one-pass variance:
+// deviations from a value of the channel do not cancel when its mean is far from zero);
+// cnt counts the values summed.  With MASKED, values of pixels past the step (own: !use,
+// partner: !use_p) are left out.  The bf16 results go to staging row px (16-byte chunk
+// c of a row at position c ^ perm(px)).
 template <bool MASKED>
-__device__ __forceinline__ void epilogue(const f32x16 &acc, bool use, uint8_t *stg, int px, int j, int hi,
-                                         float (&s1)[8], float (&s2)[8])
+__device__ __forceinline__ void epilogue(const f32x16 &acc, bool use, bool use_p, bool first, uint8_t *stg, int px,
+                                         int j, int hi, float (&c)[8], float (&s1)[8], float (&s2)[8], float &cnt)
 {
     float v[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) v[c] = acc[c];
+    for (int k = 0; k < 16; ++k) v[k] = acc[k];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
         *(u32x2 *)(stg + px * PXB + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
             u32x2{pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-    if constexpr (MASKED) {
+    const bool even = (px & 16) == 0;
+    const bool ua = even ? use : use_p, ub = even ? use_p : use;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) v[c] = use ? v[c] : 0.f;
+    for (int i = 0; i < 8; ++i) swap_rows(v[i], v[i + 8]);
+    if (first) {
+        // a pixel past the step holds the conv output of the step's first pixel: a value
+        // of the channel all the same
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = v[i];
     }
-    // after the swap both values of pair i are the same channel: their sum goes to s1,
-    // their squares to s2 (two fused multiply-adds)
+    // both values of pair i are the same channel: their deviations go to s1, their
+    // squares to s2 (two fused multiply-adds)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        swap_rows(v[i], v[i + 8]);
-        s1[i] += v[i] + v[i + 8];
-        s2[i] = fmaf(v[i + 8], v[i + 8], fmaf(v[i], v[i], s2[i]));
+        float a = v[i] - c[i], b = v[i + 8] - c[i];
+        if constexpr (MASKED) {
+            a = ua ? a : 0.f;
+            b = ub ? b : 0.f;
+        }
+        s1[i] += a + b;
+        s2[i] = fmaf(b, b, fmaf(a, a, s2[i]));
     }
+    if constexpr (MASKED)
+        cnt += (float)ua + (float)ub;
+    else
+        cnt += 2.f;
 }
 
 // A staged step awaiting its stores: d[k] holds run k of the half being stored (a run is
@@ -333,12 +355,14 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     }
 
     // Per-lane running statistics (layout: see epilogue).
-    float s1[8], s2[8];
+    float c[8], s1[8], s2[8], cnt = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        c[i] = 0.f;
         s1[i] = 0.f;
         s2[i] = 0.f;
     }
+    bool first = true;   // wave-uniform: the wave's first pixel block sets the shifts
 
     Staged prev;          // the previous step, staged in buffer pbuf
     prev.nq = 0;
@@ -459,9 +483,10 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                     KLoop<decltype(side)>{wf, ba, acc, side}.run();
                 }
                 if (full)
-                    epilogue<false>(acc, use, stg, px, j, his, s1, s2);
+                    epilogue<false>(acc, use, true, first, stg, px, j, his, c, s1, s2, cnt);
                 else
-                    epilogue<true>(acc, use, stg, px, j, his, s1, s2);
+                    epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, his, c, s1, s2, cnt);
+                first = false;
             }
 
             // The staged rows must have landed before any wave reads them: wait for this
@@ -480,32 +505,73 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     for (int k = 0; k < 4; ++k) store_staged(prev, j, k, lane);
     __syncthreads();   // every wave is done with the staging buffers and the ring
 
-    // Cross-lane sum through LDS.  st[f][tid] holds entry f = 8*which + i of the lane's
-    // [s1 | s2].
-    float *st = (float *)lds;             // [16][NT]
+    // Combination of the lanes' statistics (count n, mean = c + s1/n, M2 = s2 - s1^2/n)
+    // by the law of total variance, mean = sum n_l mean_l / n, M2 = sum [M2_l + n_l
+    // (mean_l - mean)^2]: first over the 16 lanes of a 16-lane row, which hold the same
+    // channels (butterflies of lane shuffles, fp32; the two operands of every addition
+    // are the same at both lanes, so the sums are identical across the row), then over
+    // the 4 waves of a channel half in fp64, one thread per channel.  st[w][r][f]: wave w,
+    // 16-lane row r, f = 0: count, 1 + i: mean of pair i, 9 + i: M2 of pair i.
+    float *st = (float *)lds;             // [NW][4][17]
+    {
+        const float rc = cnt > 0.f ? 1.f / cnt : 0.f;
+        float ml[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        st[i * NT + tid] = s1[i];
-        st[(8 + i) * NT + tid] = s2[i];
+        for (int i = 0; i < 8; ++i) {
+            ml[i] = c[i] + s1[i] * rc;
+            q[i] = fmaxf(s2[i] - s1[i] * s1[i] * rc, 0.f);
+        }
+        auto rowsum = [](float v) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+            return v;
+        };
+        const float nr = rowsum(cnt);
+        const float rn = nr > 0.f ? 1.f / nr : 0.f;
+        float mr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mr[i] = rowsum(cnt * ml[i]) * rn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float d = ml[i] - mr[i];
+            q[i] = rowsum(fmaf(cnt * d, d, q[i]));
+        }
+        if ((lane & 15) == 0) {
+            float *e = st + (wave * 4 + (lane >> 4)) * 17;
+            e[0] = nr;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[1 + i] = mr[i];
+                e[9 + i] = q[i];
+            }
+        }
     }
     __syncthreads();
-    // Thread (which, k) sums channel k = 32j + 8g + 4h + e over the 4 waves of half j x
-    // the 16 lanes that hold it (hi == h, (l / 16) % 2 == g / 2; entry i = 4 (g % 2) + e),
-    // in a fixed order.
-    if (tid < 2 * HK) {
-        const int which = tid >> 6, k = tid & 63;
+    if (tid < HK) {
+        // channel k = 32j + 8g + 4h + e lives in waves 4j .. 4j + 3, 16-lane row 2h + g/2,
+        // pair i = 4 (g % 2) + e
+        const int k = tid;
         const int jk = k >> 5, g = (k >> 3) & 3, h = (k >> 2) & 1, e = k & 3;
-        const f32x4 *row =
-            (const f32x4 *)(st + (8 * which + 4 * (g & 1) + e) * NT + 256 * jk + 32 * h + 16 * (g >> 1));
-        float a = 0.f;
+        const int r = 2 * h + (g >> 1), i = 4 * (g & 1) + e;
+        double n = 0.0, sm = 0.0;
 #pragma unroll
-        for (int w = 0; w < NSIMD; ++w)
+        for (int w = 0; w < NSIMD; ++w) {
+            const float *en = st + ((4 * jk + w) * 4 + r) * 17;
+            n += (double)en[0];
+            sm += (double)en[0] * (double)en[1 + i];
+        }
+        const double mean = n > 0.0 ? sm / n : 0.0;
+        double m2 = 0.0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 q = row[16 * w + i];
-                a += (q[0] + q[1]) + (q[2] + q[3]);
-            }
-        p.partials[(size_t)blockIdx.x * 2 * HK + which * HK + k] = a;
+        for (int w = 0; w < NSIMD; ++w) {
+            const float *en = st + ((4 * jk + w) * 4 + r) * 17;
+            const double d = (double)en[1 + i] - mean;
+            m2 += (double)en[9 + i] + (double)en[0] * d * d;
+        }
+        float *row = p.partials + (size_t)blockIdx.x * 2 * HK;
+        row[k] = (float)mean;
+        row[HK + k] = (float)m2;
+        if (k == 0) p.partials[(size_t)gridDim.x * 2 * HK + blockIdx.x] = (float)n;
     }
 }
 

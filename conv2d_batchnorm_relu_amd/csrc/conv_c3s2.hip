@@ -35,7 +35,7 @@ struct C3Params {
     const uint16_t *x;      // N x H x W x 3
     const uint16_t *wexp;   // 64 x R x 8 x 4 (zero-padded filter)
     uint16_t *z;            // N x P x Q x 64
-    float *partials;        // [gridDim.x][2][64]
+    float *partials;        // [gridDim.x][2][64] means and M2, then [gridDim.x] counts
     int N, H, W, R, ph, pw, P, Q;
     int bands;              // ceil(P / TP)
     int LW;                 // staged pixels per input row (zero columns included)
@@ -172,14 +172,12 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
     // chunk c of band pixel px at (c ^ perm(px)) << 4, and leaves as 1 KB runs of whole
     // 128-byte pixel rows: storing straight from the MFMA layout touches 32 cache lines per
     // instruction with 16 bytes each, which the memory pipeline processes line by line.
-    float s1[4][4], s2[4][4];
+    // Statistics, first pass: per-lane channel sums over the valid pixels.
+    float s1[4][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s1[g][e] = 0.f;
-            s2[g][e] = 0.f;
-        }
+        for (int e = 0; e < 4; ++e) s1[g][e] = 0.f;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
@@ -191,16 +189,16 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
             const float a2 = acc[u][4 * g + 2], a3 = acc[u][4 * g + 3];
             *(u32x2 *)(lds + px * 128 + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
                 u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-            s1[g][0] += a0; s2[g][0] = fmaf(a0, a0, s2[g][0]);
-            s1[g][1] += a1; s2[g][1] = fmaf(a1, a1, s2[g][1]);
-            s1[g][2] += a2; s2[g][2] = fmaf(a2, a2, s2[g][2]);
-            s1[g][3] += a3; s2[g][3] = fmaf(a3, a3, s2[g][3]);
+            s1[g][0] += a0;
+            s1[g][1] += a1;
+            s1[g][2] += a2;
+            s1[g][3] += a3;
         }
     }
     __syncthreads();
+    // The band's rows are contiguous in z (NHWC): npx pixels from pixel (n, p0, 0).
+    const int npx = min(TP, p.P - p0) * Q;
     {
-        // The band's rows are contiguous in z (NHWC): npx pixels from pixel (n, p0, 0).
-        const int npx = min(TP, p.P - p0) * Q;
         const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
             p.z + ((size_t)n * p.P + p0) * Q * KOUT, 0, npx * KOUT * 2, 0x00020000);
         // sc1 without nt: measured, the z lines then still sit in the last-level cache for
@@ -213,22 +211,14 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
         }
     }
 
-    // Cross-lane sum through LDS, once every wave has read its z runs:
-    // st[f][tid], f = 16*which + 4*g + e for channel 32j + 8g + 4hi + e.
+    // Cross-lane reductions through LDS, once every wave has read its z runs:
+    // st[f][tid], f = 4*g + e for channel 32j + 8g + 4hi + e.  Thread (f, jj, h) of the
+    // first 128 sums the 64 lanes of channel block jj with hi == h (waves 2jj and 2jj + 1
+    // x 32 lanes) in a fixed order.
     __syncthreads();
-    float *st = (float *)lds;   // 32 x NT floats = 32 KB
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            st[(4 * g + e) * NT + tid] = s1[g][e];
-            st[(16 + 4 * g + e) * NT + tid] = s2[g][e];
-        }
-    __syncthreads();
-    // Thread (f, jj, h) sums the 64 lanes of channel block jj with hi == h: waves 2jj and
-    // 2jj + 1 x 32 lanes, fixed order.
-    if (tid < 128) {
-        const int f = tid >> 2, jj = (tid >> 1) & 1, h = tid & 1;
+    float *st = (float *)lds;            // 16 x NT floats = 16 KB
+    float *bmean = st + 16 * NT;         // the band's 64 channel means
+    auto reduce = [&](int f, int jj, int h) {
         float a = 0.f;
 #pragma unroll
         for (int w = 2 * jj; w < 2 * jj + 2; ++w) {
@@ -239,10 +229,39 @@ __global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
                 a += (q[0] + q[1]) + (q[2] + q[3]);
             }
         }
-        const int which = f >> 4, ge = f & 15;
-        const int k = 32 * jj + 8 * (ge >> 2) + 4 * h + (ge & 3);
-        p.partials[(size_t)blockIdx.x * 2 * KOUT + which * KOUT + k] = a;
+        return a;
+    };
+    const int rf = tid >> 2, rjj = (tid >> 1) & 1, rh = tid & 1;      // reducing thread's role
+    const int rk = 32 * rjj + 8 * (rf >> 2) + 4 * rh + (rf & 3);      // its channel
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[(4 * g + e) * NT + tid] = s1[g][e];
+    __syncthreads();
+    if (tid < 64) bmean[rk] = reduce(rf, rjj, rh) / (float)npx;
+    __syncthreads();
+    // Second pass: squared deviations of the valid pixels from the band's means.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 m4 = *(const f32x4 *)(bmean + 32 * j + 8 * g + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int u = 0; u < UPW; ++u) {
+                const float d = acc[u][4 * g + e] - m4[e];
+                s2 = valid[u] ? fmaf(d, d, s2) : s2;
+            }
+            st[(4 * g + e) * NT + tid] = s2;
+        }
     }
+    __syncthreads();
+    if (tid < 64) {
+        float *row = p.partials + (size_t)blockIdx.x * 2 * KOUT;
+        row[rk] = bmean[rk];
+        row[KOUT + rk] = reduce(rf, rjj, rh);
+    }
+    if (tid == 0) p.partials[(size_t)gridDim.x * 2 * KOUT + blockIdx.x] = (float)npx;
 }
 
 int c3_bands(const ConvGeom &g) { return (g.P + TP - 1) / TP; }

@@ -11,9 +11,10 @@
 //
 // Epilogues (one template parameter):
 //   EPI_STATS      store z as bf16 and, from the fp32 accumulators, the per-channel
-//                  sum and sum of squares of this tile's rows -- the conv + genstats step
-//                  of the CBR page's training forward (section 4.1), which spares the
-//                  statistics pass a re-read of z;
+//                  statistics of this tile's rows (count, mean, and M2 = the sum of
+//                  squared deviations from that mean, by two passes over the registers)
+//                  -- the conv + genstats step of the CBR page's training forward
+//                  (section 4.1), which spares the statistics pass a re-read of z;
 //   EPI_BIAS_RELU  y = max(acc + bias, 0) -- the folded-BN inference form (CBR page
 //                  sections 2 and 6; the TileLang page's fused-ReLU epilogue);
 //   EPI_PLAIN      store acc as bf16 (data gradient).
@@ -248,24 +249,18 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
 
     // Epilogue.  Accumulator layout of v_mfma_f32_32x32x16: lane l holds column
     // (l & 31) and rows 8*(v/4) + 4*(l >> 5) + v%4, v = 0..15, of each 32 x 32 block.
+    // Statistics, first pass: the column sums of the tile (rows past M hold zeros).
+    const int nrows = min(BM, g.M - m0);
     if constexpr (EPI == EPI_STATS) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            float s1 = 0.f, s2 = 0.f;
+            float s1 = 0.f;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float a = acc[i][j][v];
-                    s1 += a;
-                    s2 += a * a;
-                }
+                for (int v = 0; v < 16; ++v) s1 += acc[i][j][v];
             s1 += __shfl_xor(s1, 32);
-            s2 += __shfl_xor(s2, 32);
-            if (lane < 32) {
-                sstat[wm][0][wn * WN + 32 * j + lane] = s1;
-                sstat[wm][1][wn * WN + 32 * j + lane] = s2;
-            }
+            if (lane < 32) sstat[wm][0][wn * WN + 32 * j + lane] = s1;
         }
     }
     float bcol[NJ];
@@ -288,11 +283,23 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
                 so[row * LDO + col] = (uint16_t)f32_to_bf16_bits(val);
             }
     __syncthreads();
+    // Second pass: the squared deviations of the valid rows from the tile's column means.
+    auto tile_mean = [&](int col) { return (sstat[0][0][col] + sstat[1][0][col]) / (float)nrows; };
     if constexpr (EPI == EPI_STATS) {
-        if (tid < BN && n0 + tid < g.K) {
-            float *pt = prm.partials + (size_t)tile_m * 2 * g.K;
-            pt[n0 + tid] = sstat[0][0][tid] + sstat[1][0][tid];
-            pt[g.K + n0 + tid] = sstat[0][1][tid] + sstat[1][1][tid];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float mt = tile_mean(wn * WN + 32 * j + (lane & 31));
+            float s2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const float d = acc[i][j][v] - mt;
+                    s2 = row < nrows ? fmaf(d, d, s2) : s2;
+                }
+            s2 += __shfl_xor(s2, 32);
+            if (lane < 32) sstat[wm][1][wn * WN + 32 * j + lane] = s2;
         }
     }
     constexpr int CPRO = BN / 8;
@@ -305,6 +312,16 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
         } else {   // output rows not 16-byte aligned (data gradient with C % 8 != 0)
             for (int e = 0; e < 8 && k + e < g.K; ++e) prm.out[(size_t)m * g.K + k + e] = so[row * LDO + ch * 8 + e];
         }
+    }
+    if constexpr (EPI == EPI_STATS) {
+        // Row tile_m of the partials: means, M2, and (after all rows) the row's count.
+        __syncthreads();
+        if (tid < BN && n0 + tid < g.K) {
+            float *pt = prm.partials + (size_t)tile_m * 2 * g.K;
+            pt[n0 + tid] = tile_mean(tid);
+            pt[g.K + n0 + tid] = sstat[0][1][tid] + sstat[1][1][tid];
+        }
+        if (tile_n == 0 && tid == 0) prm.partials[(size_t)gridDim.x * 2 * g.K + tile_m] = (float)nrows;
     }
 }
 

@@ -20,9 +20,10 @@
 //     chunk's first loads.
 //   * Results leave through an LDS staging tile as whole 16-byte chunks of contiguous
 //     output rows.
-// Epilogues as in conv_fprop.hip: EPI_STATS (z + per-channel sum and sum of squares of
-// the fp32 accumulators, the CBR page's conv + genstats, section 4.1), EPI_BIAS_RELU (the
-// folded-BN inference form, CBR page sections 2 and 6), EPI_PLAIN (data gradient).
+// Epilogues as in conv_fprop.hip: EPI_STATS (z + per-channel count, mean and M2 of each
+// pixel chunk's fp32 accumulators, two passes over the registers: the CBR page's conv +
+// genstats, section 4.1), EPI_BIAS_RELU (the folded-BN inference form, CBR page sections
+// 2 and 6), EPI_PLAIN (data gradient).
 #include <type_traits>
 
 #include "cbr_launch.h"
@@ -46,6 +47,7 @@ struct IgParams {
     int ksteps;        // Kg / BK slices per chunk
     int rows_per_wg;   // contiguous output pixels per workgroup
     int ntn;           // K / BN
+    int maxmc;         // pixel chunks per workgroup at most (statistics rows per workgroup)
 };
 
 constexpr uint32_t OOB = 0x80000000u;   // past the end of every buffer (sizes < 2^31)
@@ -167,8 +169,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
     const int nchunk = nmc * p.ntn;
     const int total = nchunk * p.ksteps;
 
+    // Statistics rows: row blockIdx.x * maxmc + mc holds pixel chunk mc of this workgroup;
+    // the rows of chunks it does not have are zeros (count 0).
+    float *const counts = p.partials + (size_t)gridDim.x * p.maxmc * 2 * p.K;
     if constexpr (EPI == EPI_STATS) {
-        for (int i = tid; i < 2 * p.K; i += NT) stat_acc[i] = 0.f;
+        for (int mc = nmc; mc < p.maxmc; ++mc) {
+            const int row = blockIdx.x * p.maxmc + mc;
+            for (int i = tid; i < 2 * p.K; i += NT) p.partials[(size_t)row * 2 * p.K + i] = 0.f;
+            if (tid == 0) counts[row] = 0.f;
+        }
     }
 
     // ---- slice loads: instruction u (rows RPI*u .. RPI*u + RPI - 1) is issued by wave
@@ -289,27 +298,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         asm volatile("" : "+v"(ln));
         const int el32 = ln & 31, ehi = ln >> 5;
         if constexpr (EPI == EPI_STATS) {
-            // Per lane: sums over its pixel blocks (pixels past the range are zeros);
-            // then over the 32 pixel lanes and the WGM pixel-wave rows through LDS.
+            // Per channel, over the chunk's nvalid pixels: first the means (per lane over its
+            // pixel blocks -- pixels past the range are zeros --, then over the 32 pixel lanes
+            // and the WGM pixel-wave rows through LDS), then the squared deviations from
+            // them (valid pixels only), reduced the same way.
             float *scr = (float *)lds;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float t1 = 0.f, t2 = 0.f;
-#pragma unroll
-                    for (int i = 0; i < MI; ++i) {
-                        const float a = acc[i][j][v];
-                        t1 += a;
-                        t2 = fmaf(a, a, t2);
-                    }
-                    scr[(wave * NF + 2 * (16 * j + v)) * 64 + ln] = t1;
-                    scr[(wave * NF + 2 * (16 * j + v) + 1) * 64 + ln] = t2;
-                }
-            barrier();
-            for (int o = tid; o < 2 * BN; o += NT) {
-                // o = 2 * channel + stat; channel = wn'*32NJ + 32j + 8(v/4) + 4h + v%4
-                const int st = o & 1, ch = o >> 1;
+            float *cmean = stat_acc;   // BN channel means of this chunk
+            auto reduce = [&](int st, int ch) {
+                // ch = wn'*32NJ + 32j + 8(v/4) + 4h + v%4
                 const int wn2 = ch / (32 * NJ), cj = ch - wn2 * 32 * NJ;
                 const int j = cj >> 5, cr = cj & 31;
                 const int v = ((cr >> 3) << 2) | (cr & 3), h = (cr >> 2) & 1;
@@ -322,7 +318,44 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
                         sum += (q4[0] + q4[1]) + (q4[2] + q4[3]);
                     }
                 }
-                stat_acc[st * p.K + n0 + ch] += sum;
+                return sum;
+            };
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float t1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) t1 += acc[i][j][v];
+                    scr[(wave * NF + 2 * (16 * j + v)) * 64 + ln] = t1;
+                }
+            barrier();
+            for (int ch = tid; ch < BN; ch += NT) cmean[ch] = reduce(0, ch) / (float)nvalid;
+            barrier();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 m4 = *(const f32x4 *)(cmean + wn * 32 * NJ + 32 * j + 8 * g + 4 * ehi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float t2 = 0.f;
+#pragma unroll
+                        for (int i = 0; i < MI; ++i) {
+                            const float d = acc[i][j][4 * g + e] - m4[e];
+                            t2 = wm * 32 * MI + 32 * i + el32 < nvalid ? fmaf(d, d, t2) : t2;
+                        }
+                        scr[(wave * NF + 2 * (16 * j + 4 * g + e) + 1) * 64 + ln] = t2;
+                    }
+                }
+            barrier();
+            {
+                const int row = blockIdx.x * p.maxmc + mc;
+                for (int ch = tid; ch < BN; ch += NT) {
+                    p.partials[(size_t)row * 2 * p.K + n0 + ch] = cmean[ch];
+                    p.partials[(size_t)row * 2 * p.K + p.K + n0 + ch] = reduce(1, ch);
+                }
+                if (n0 == 0 && tid == 0) counts[row] = (float)nvalid;
             }
             barrier();
         }
@@ -461,11 +494,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         }
     }
 
-    if constexpr (EPI == EPI_STATS) {
-        vm_wait<0>();
-        barrier();
-        for (int i = tid; i < 2 * p.K; i += NT) p.partials[(size_t)blockIdx.x * 2 * p.K + i] = stat_acc[i];
-    }
 }
 
 struct IgConfig {
@@ -496,7 +524,7 @@ size_t ig_lds_bytes(const ConvGeom &g, int epi)
     const size_t stage = (size_t)c.nstage * (c.bm() + c.bn()) * 2 * c.bk;
     const size_t scr = epi == EPI_STATS ? (size_t)c.nw() * 64 * c.nj * 32 * 4 : 0;
     const size_t stg = std::max((size_t)c.bm() * 2 * c.bn(), scr);
-    const size_t stats = epi == EPI_STATS ? (size_t)2 * g.K * 4 : 0;
+    const size_t stats = epi == EPI_STATS ? (size_t)c.bn() * 4 : 0;   // a chunk's channel means
     return std::max(stage, stg) + stats;
 }
 
@@ -535,7 +563,9 @@ bool igemm_eligible(const ConvGeom &g, int epi)
     return ig_lds_bytes(g, epi) <= 160 * 1024;
 }
 
-int igemm_partial_rows(const ConvGeom &g) { return ig_grid(g); }
+int ig_maxmc(const ConvGeom &g) { return (ig_rows_per_wg(g) + ig_config(g).bm() - 1) / ig_config(g).bm(); }
+
+int igemm_partial_rows(const ConvGeom &g) { return ig_grid(g) * ig_maxmc(g); }
 
 hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w, const float *bias,
                              uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
@@ -555,6 +585,7 @@ hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, cons
     prm.ksteps = g.Kg / c.bk;
     prm.rows_per_wg = ig_rows_per_wg(g);
     prm.ntn = g.K / c.bn();
+    prm.maxmc = ig_maxmc(g);
     const int grid = ig_grid(g);
     const size_t lds = ig_lds_bytes(g, epi);
     if (c.wgm == 1) {
