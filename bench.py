@@ -168,7 +168,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
     def shape_of(g):
-        return cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.pad)
+        return cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.sh, g.ph, stride_w=g.sw, pad_w=g.pw)
 
     def make_event():
         # torch creates the underlying hipEvent_t on first record; the library then
@@ -304,6 +304,16 @@ def main():
                         "kernels": [kernel_entry("bn_fold", st4[0], ib["bn_fold"], 0),
                                     kernel_entry("conv_fprop_bias_relu", st4[1], ib["conv_fprop_bias_relu"],
                                                  conv_flops(g4))]}
+        log("conv + bias + relu workload")
+
+        def cbr_step(events):
+            cbr.cbr_conv2d_bias_relu(sp4, t4["x"], t4["w"], t4["b"], t4["y"], events=events)
+
+        ms4c, st4c, _ = timed(cbr_step, 2, steps, 5)
+        aux["conv_bias_relu"] = {"workload": "Conv2D + bias + ReLU, no BN: N256 28x28 C128->K128 3x3 s1 p1",
+                                 "ms": round(ms4c, 5), "tflops": round(conv_flops(g4) / (ms4c * 1e-3) / 1e12, 2),
+                                 "kernels": [kernel_entry("conv_bias_relu", st4c[0], ib["conv_fprop_bias_relu"],
+                                                          conv_flops(g4))]}
         del t4
         log("backward workload")
         wl5, d5 = draw_workload("s4_bwd")

@@ -18,6 +18,7 @@ import os
 
 __all__ = ["CbrError", "CbrShape", "make_shape", "cbr_status_str", "cbr_output_hw", "cbr_mask_words",
            "cbr_workspace_bytes", "cbr_forward_train", "cbr_forward_infer", "cbr_backward",
+           "cbr_conv2d_bias_relu", "cbr_conv2d_bias",
            "CBR_OP_TRAIN", "CBR_OP_INFER", "CBR_OP_BWD", "library_path"]
 
 CBR_OP_TRAIN, CBR_OP_INFER, CBR_OP_BWD = 0, 1, 2
@@ -75,6 +76,12 @@ def _load():
     lib.cbr_forward_infer_ev.restype = ctypes.c_int
     lib.cbr_backward_ev.argtypes = lib.cbr_backward.argtypes + [P]
     lib.cbr_backward_ev.restype = ctypes.c_int
+    for name in ("cbr_conv2d_bias_relu", "cbr_conv2d_bias"):
+        fn, fe = getattr(lib, name), getattr(lib, name + "_ev")
+        fn.argtypes = [S, P, P, P, P, P]
+        fn.restype = ctypes.c_int
+        fe.argtypes = fn.argtypes + [P]
+        fe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -201,3 +208,20 @@ def cbr_backward(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd,
         _check(_load().cbr_backward(*args), f)
     else:
         _check(_load().cbr_backward_ev(*args, _events(events)), "cbr_backward_ev")
+
+
+def _conv_bias(name, shape, x, w, bias, y, stream, events):
+    args = (_sp(shape), _ptr(x, 2, "x", name), _ptr(w, 2, "w", name), _ptr(bias, 4, "bias", name),
+            _ptr(y, 2, "y", name), _stream(stream))
+    if events is None:
+        _check(getattr(_load(), name)(*args), name)
+    else:
+        _check(getattr(_load(), name + "_ev")(*args, _events(events)), name + "_ev")
+
+
+def cbr_conv2d_bias_relu(shape, x, w, bias, y, stream=None, events=None):
+    _conv_bias("cbr_conv2d_bias_relu", shape, x, w, bias, y, stream, events)
+
+
+def cbr_conv2d_bias(shape, x, w, bias, y, stream=None, events=None):
+    _conv_bias("cbr_conv2d_bias", shape, x, w, bias, y, stream, events)

@@ -246,6 +246,46 @@ int cbr_forward_infer(const cbr_shape *shape, const uint16_t *x, const uint16_t 
                                 ws_bytes, stream, nullptr);
 }
 
+// Conv2D + bias (+ ReLU) without batch normalisation: one convolution launch with the
+// bias (and ReLU) epilogue.
+static int conv_bias_act(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias, bool relu,
+                         uint16_t *y, void *stream, void *const *events)
+{
+    ConvGeom g;
+    int st = make_geom(shape, &g);
+    if (st != CBR_OK) return st;
+    if (any_null(x, w, y)) return CBR_E_NULL;
+    if (!all_aligned(x, w, y) || (bias && !aligned16(bias))) return CBR_E_ALIGN;
+    if (launch_conv_fprop(g, relu ? EPI_BIAS_RELU : EPI_BIAS, x, w, bias, y, nullptr, (hipStream_t)stream,
+                          ev(events, 0), ev(events, 1)) != hipSuccess)
+        return CBR_E_HIP;
+    return CBR_OK;
+}
+
+int cbr_conv2d_bias_relu_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias,
+                            uint16_t *y, void *stream, void *const *events)
+{
+    return conv_bias_act(shape, x, w, bias, true, y, stream, events);
+}
+
+int cbr_conv2d_bias_relu(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias, uint16_t *y,
+                         void *stream)
+{
+    return conv_bias_act(shape, x, w, bias, true, y, stream, nullptr);
+}
+
+int cbr_conv2d_bias_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias, uint16_t *y,
+                       void *stream, void *const *events)
+{
+    return conv_bias_act(shape, x, w, bias, false, y, stream, events);
+}
+
+int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias, uint16_t *y,
+                    void *stream)
+{
+    return conv_bias_act(shape, x, w, bias, false, y, stream, nullptr);
+}
+
 int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const uint16_t *z,
                     const uint32_t *relu_mask, const uint16_t *dy, const float *gamma, const float *saved_mean,
                     const float *saved_invstd, uint16_t *dz, float *dgamma, float *dbeta, float *dw,

@@ -17,7 +17,10 @@
 
 namespace cbr {
 
-enum ConvEpilogue { EPI_STATS = 0, EPI_BIAS_RELU = 1, EPI_PLAIN = 2 };
+// Conv epilogues: statistics (training), bias + ReLU (folded-BN inference, and the plain
+// Conv2D + ReLU), plain (data gradient), bias without activation.  A NULL bias reads as
+// zeros.
+enum ConvEpilogue { EPI_STATS = 0, EPI_BIAS_RELU = 1, EPI_PLAIN = 2, EPI_BIAS = 3 };
 
 // Arguments of the BN finalize: per-channel inputs and outputs (float [K] each).
 struct BnFinalizeArgs {

@@ -17,7 +17,9 @@
 //                  (section 4.1), which spares the statistics pass a re-read of z;
 //   EPI_BIAS_RELU  y = max(acc + bias, 0) -- the folded-BN inference form (CBR page
 //                  sections 2 and 6; the TileLang page's fused-ReLU epilogue);
-//   EPI_PLAIN      store acc as bf16 (data gradient).
+//   EPI_PLAIN      store acc as bf16 (data gradient);
+//   EPI_BIAS       y = acc + bias (Conv2D with bias, no activation).
+// A NULL bias reads as zeros.
 // The im2col tiling follows the TileLang page's basic convolution (grid over output
 // pixel tiles x output channel tiles, a pipelined loop over ceil(KH*KW*C / block_K)).
 #include "cbr_launch.h"
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int col = n0 + wn * WN + 32 * j + (lane & 31);
-        bcol[j] = (EPI == EPI_BIAS_RELU && col < g.K) ? prm.bias[col] : 0.f;
+        bcol[j] = ((EPI == EPI_BIAS_RELU || EPI == EPI_BIAS) && prm.bias && col < g.K) ? prm.bias[col] : 0.f;
     }
     uint16_t *so = smem;
 #pragma unroll
@@ -280,6 +282,7 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
                 const int col = wn * WN + 32 * j + (lane & 31);
                 float val = acc[i][j][v];
                 if constexpr (EPI == EPI_BIAS_RELU) val = fmaxf(val + bcol[j], 0.f);
+                if constexpr (EPI == EPI_BIAS) val += bcol[j];
                 so[row * LDO + col] = (uint16_t)f32_to_bf16_bits(val);
             }
     __syncthreads();
@@ -332,6 +335,7 @@ hipError_t launch_epi(int epi, const ConvParams &prm, dim3 grid, hipStream_t st,
     case EPI_STATS: return launch(conv_fprop_kernel<BM, BN, MODE, EPI_STATS>, grid, dim3(NT), 0, st, e0, e1, prm);
     case EPI_BIAS_RELU:
         return launch(conv_fprop_kernel<BM, BN, MODE, EPI_BIAS_RELU>, grid, dim3(NT), 0, st, e0, e1, prm);
+    case EPI_BIAS: return launch(conv_fprop_kernel<BM, BN, MODE, EPI_BIAS>, grid, dim3(NT), 0, st, e0, e1, prm);
     default: return launch(conv_fprop_kernel<BM, BN, MODE, EPI_PLAIN>, grid, dim3(NT), 0, st, e0, e1, prm);
     }
 }

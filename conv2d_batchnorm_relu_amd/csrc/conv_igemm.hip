@@ -23,7 +23,8 @@
 // Epilogues as in conv_fprop.hip: EPI_STATS (z + per-channel count, mean and M2 of each
 // pixel chunk's fp32 accumulators, two passes over the registers: the CBR page's conv +
 // genstats, section 4.1), EPI_BIAS_RELU (the folded-BN inference form, CBR page sections
-// 2 and 6), EPI_PLAIN (data gradient).
+// 2 and 6, and the TileLang page's Conv2D + ReLU), EPI_PLAIN (data gradient), EPI_BIAS
+// (Conv2D + bias).  A NULL bias reads as zeros.
 #include <type_traits>
 
 #include "cbr_launch.h"
@@ -360,12 +361,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
             barrier();
         }
         float bj[NJ][16];
-        if constexpr (EPI == EPI_BIAS_RELU) {
+        if constexpr (EPI == EPI_BIAS_RELU || EPI == EPI_BIAS) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const f32x4 b4 = *(const f32x4 *)(p.bias + n0 + wn * 32 * NJ + 32 * j + 8 * g + 4 * ehi);
+                    const f32x4 b4 = p.bias ? *(const f32x4 *)(p.bias + n0 + wn * 32 * NJ + 32 * j + 8 * g + 4 * ehi)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) bj[j][4 * g + e] = b4[e];
                 }
@@ -383,6 +385,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
                     for (int e = 0; e < 4; ++e) {
                         a[e] = acc[i][j][4 * g + e];
                         if constexpr (EPI == EPI_BIAS_RELU) a[e] = fmaxf(a[e] + bj[j][4 * g + e], 0.f);
+                        if constexpr (EPI == EPI_BIAS) a[e] += bj[j][4 * g + e];
                     }
                     const int cc = wn * 4 * NJ + 4 * j + g;
                     lds_write8(sbase + px * STG_ROW + ((cc ^ (px & 15)) << 4) + 8 * ehi,
@@ -547,6 +550,7 @@ hipError_t ig_launch_cfg(int epi, const IgParams &prm, int grid, size_t lds, hip
     case EPI_STATS: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_STATS>(prm, grid, lds, st, e0, e1);
     case EPI_BIAS_RELU:
         return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_BIAS_RELU>(prm, grid, lds, st, e0, e1);
+    case EPI_BIAS: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_BIAS>(prm, grid, lds, st, e0, e1);
     default: return ig_launch_one<MI, NJ, WGM, WGN, BK, NSTAGE, EPI_PLAIN>(prm, grid, lds, st, e0, e1);
     }
 }

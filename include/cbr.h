@@ -153,6 +153,25 @@ int cbr_backward(const cbr_shape *shape,
                  void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Conv2D + bias + ReLU without batch normalisation ([TL] "fused ReLU" section: the ReLU
+ * applied in the convolution's epilogue, before the result leaves the chip):
+ *   y = max(conv(x, w) + bias, 0)                                  bf16 [N,P,Q,K] (out)
+ * x: bf16 NHWC [N,H,W,C]; w: bf16 KRSC [K,R,S,C]; bias: float [K], may be NULL (read as
+ * zero).  No workspace.  Shape limits and errors as for the other calls.
+ */
+int cbr_conv2d_bias_relu(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias,
+                         uint16_t *y, void *stream);
+
+/*
+ * Conv2D + bias without activation ([TL] basic convolution with a bias epilogue; the
+ * convolution of [CBR] section 2, y = conv(x, W, b)):
+ *   y = conv(x, w) + bias                                          bf16 [N,P,Q,K] (out)
+ * Arguments as for cbr_conv2d_bias_relu.
+ */
+int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias,
+                    uint16_t *y, void *stream);
+
+/*
  * Timed variants for profiling: identical to the calls above, and in addition record
  * caller-created hipEvent_t handles (passed as void*) at the start of the first kernel
  * and the end of the last kernel of each stage (taken from the kernels' own dispatch
@@ -163,6 +182,7 @@ int cbr_backward(const cbr_shape *shape,
  *   infer:  [0,1] fold, [2,3] convolution + bias + ReLU                     (4 events)
  *   bwd:    [0,1] BN backward (reduce, finalize, dz), [2,3] weight gradient,
  *           [4,5] data gradient (recorded back to back when dx is NULL)    (6 events)
+ *   conv2d_bias(_relu): [0,1] the convolution                             (2 events)
  */
 int cbr_forward_train_ev(const cbr_shape *shape,
                          const uint16_t *x, const uint16_t *w,
@@ -187,6 +207,12 @@ int cbr_backward_ev(const cbr_shape *shape,
                     const float *gamma, const float *saved_mean, const float *saved_invstd,
                     uint16_t *dz, float *dgamma, float *dbeta, float *dw, uint16_t *dx,
                     void *workspace, size_t ws_bytes, void *stream, void *const *events);
+
+int cbr_conv2d_bias_relu_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias,
+                            uint16_t *y, void *stream, void *const *events);
+
+int cbr_conv2d_bias_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, const float *bias,
+                       uint16_t *y, void *stream, void *const *events);
 
 #ifdef __cplusplus
 }

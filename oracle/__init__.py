@@ -55,6 +55,7 @@ def _load():
         lib = ctypes.CDLL(build())
         lib.cbro_conv2d.argtypes = _GEOM + [_D, _D, _D, _D]
         lib.cbro_conv2d_at.argtypes = _GEOM + [_D, _D, _D, ctypes.c_long, _I64, _D]
+        lib.cbro_conv2d_bias_act.argtypes = _GEOM + [_D, _D, _D, ctypes.c_int, _D]
         lib.cbro_batch_stats.argtypes = [ctypes.c_long, ctypes.c_int, _D, _D, _D]
         lib.cbro_forward_train.argtypes = _GEOM + [_D, _D, _D, _D, _D, _D, ctypes.c_double,
                                                    ctypes.c_double, _D, _D, _U8, _D, _D, _D, _D, _D]
@@ -110,6 +111,16 @@ def conv2d(sp: OShape, x, w, bias=None):
     z = np.empty((sp.n, P, Q, sp.k), np.float64)
     _load().cbro_conv2d(*_g(sp), _p(x), _p(w), _p(b), _p(z))
     return z
+
+
+def conv2d_bias_act(sp: OShape, x, w, bias=None, relu=True):
+    """y = conv(x, w) + bias, then max(y, 0) when relu (fp64)."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    P, Q = out_hw(sp)
+    y = np.empty((sp.n, P, Q, sp.k), np.float64)
+    _load().cbro_conv2d_bias_act(*_g(sp), _p(x), _p(w), _p(b), int(bool(relu)), _p(y))
+    return y
 
 
 def conv2d_at(sp: OShape, x, w, idx, bias=None):

@@ -110,6 +110,23 @@ void cbro_conv2d_at(int N, int H, int W, int C, int K, int R, int S, int sh, int
 }
 
 /*
+ * Conv2D + bias with an optional ReLU, no batch normalisation:
+ *   y = conv(x, w) + bias                  (relu == 0; [CBR] section 2, y = conv(x, W, b))
+ *   y = max(conv(x, w) + bias, 0)          (relu != 0; [TL] fused ReLU section)
+ * bias may be NULL (no bias).
+ */
+void cbro_conv2d_bias_act(int N, int H, int W, int C, int K, int R, int S, int sh, int sw, int ph, int pw,
+                          const double *x, const double *w, const double *bias, int relu, double *y)
+{
+    const int P = cbro_out_size(H, ph, R, sh), Q = cbro_out_size(W, pw, S, sw);
+    cbro_conv2d(N, H, W, C, K, R, S, sh, sw, ph, pw, x, w, bias, y);
+    if (relu) {
+        const size_t total = (size_t)N * P * Q * K;
+        for (size_t i = 0; i < total; ++i) y[i] = y[i] > 0.0 ? y[i] : 0.0;
+    }
+}
+
+/*
  * Per-channel batch statistics of z viewed as [M][K]:
  *   mean_k = (1/M) sum_m z[m,k],   var_k = (1/M) sum_m (z[m,k] - mean_k)^2.
  * [BN] 2.1 (mean and variance over N x H x W per channel); [CBR] 4.2 defines

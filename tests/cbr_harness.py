@@ -118,6 +118,18 @@ def gpu_infer(g: Geometry, d: dict, eps=1e-5):
     return host_bf16(y)
 
 
+def gpu_conv_bias(g: Geometry, x, w, bias, relu):
+    """cbr_conv2d_bias_relu (relu) or cbr_conv2d_bias on host inputs; returns y."""
+    import torch
+    import conv2d_batchnorm_relu_amd as cbr
+    y = empty_bf16((g.n, g.p, g.q, g.k))
+    b = dev_f32(bias) if bias is not None else None
+    fn = cbr.cbr_conv2d_bias_relu if relu else cbr.cbr_conv2d_bias
+    fn(cshape(g), dev_bf16(x), dev_bf16(w), b, y)
+    torch.cuda.synchronize()
+    return host_bf16(y)
+
+
 def gpu_backward(g: Geometry, devt: dict, dy_host, want_dx=True, dz_out=True, dx_alias_x=False):
     import torch
     import conv2d_batchnorm_relu_amd as cbr

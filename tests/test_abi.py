@@ -148,6 +148,17 @@ def test_infer_validation(lib, over, status):
     assert _infer(shp(), **over) == status
 
 
+@pytest.mark.parametrize("name", ["cbr_conv2d_bias_relu", "cbr_conv2d_bias"])
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, FAKE, FAKE), 1), ((FAKE, FAKE, None, None), 1), ((FAKE, FAKE, FAKE + 4, FAKE), 4),
+    ((FAKE + 2, FAKE, None, FAKE), 4),
+])
+def test_conv_bias_validation(lib, name, args, status):
+    x, w, b, y = args
+    assert getattr(cbr._load(), name)(ctypes.byref(shp()), x, w, b, y, 0) == status
+    assert getattr(cbr._load(), name)(ctypes.byref(shp(k=12)), FAKE, FAKE, None, FAKE, 0) == 3
+
+
 def test_product_never_imports_oracle():
     """The package and the library sources do not reference the oracle."""
     pkg = os.path.join(ROOT, "conv2d_batchnorm_relu_amd")

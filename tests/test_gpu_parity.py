@@ -271,6 +271,42 @@ def test_train_forward_large_channel_mean(g, ratio):
     H.check_train(g, d, res, ora, y_from_stored_z=True)
 
 
+# Conv2D + bias (+ ReLU) without batch normalisation: the generic conv (small and ragged
+# channel counts, anisotropic geometry) and the large-tile conv, with and without bias.
+CONV_BIAS_GEOMS = [
+    Geometry(3, 9, 11, 16, 24, 3, 3, 1, 1),
+    Geometry(2, 13, 10, 8, 16, 7, 1, stride=1, pad=3, stride_w=2, pad_w=0),
+    Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1),
+    Geometry(3, 13, 11, 64, 256, 3, 3, 1, 1),          # large-tile conv, 224 x 256 chunks
+    Geometry(3, 160, 160, 32, 128, 3, 3, 1, 1),        # large-tile conv, 448 x 128 chunks
+    Geometry(2, 11, 15, 32, 128, 1, 3, stride=1, pad=0, stride_w=2, pad_w=1),
+]
+
+
+@pytest.mark.parametrize("relu", [True, False], ids=["relu", "linear"])
+@pytest.mark.parametrize("with_bias", [True, False], ids=["bias", "nobias"])
+@pytest.mark.parametrize("g", CONV_BIAS_GEOMS, ids=str)
+def test_conv_bias_act(g, with_bias, relu):
+    H.log(f"conv + bias (relu={relu}, bias={with_bias}) {g}")
+    d = draw(g, "infer", 23)
+    bias = d["bias"] if with_bias else None
+    y = H.gpu_conv_bias(g, d["x"], d["w"], bias, relu)
+    ref = H.oracle.conv2d_bias_act(H.oshape(g), d["x"], d["w"], bias, relu)
+    H.assert_close(y, ref, "conv + bias" + (" + relu" if relu else ""))
+    if not relu:
+        assert (y < 0).any()
+
+
+def test_conv_bias_relu_full_size():
+    """The 28x28x128 layer (N = 256, 3x3, bias) that the benchmark times, every output."""
+    g = Geometry(256, 28, 28, 128, 128, 3, 3, 1, 1)
+    d = draw(g, "infer", 24)
+    H.log(f"conv + bias + relu, full size {g}")
+    y = H.gpu_conv_bias(g, d["x"], d["w"], d["bias"], True)
+    ref = H.oracle.conv2d_bias_act(H.oshape(g), d["x"], d["w"], d["bias"], True)
+    H.assert_close(y, ref, "conv + bias + relu")
+
+
 def test_backward_dz_in_workspace_and_dx_aliasing_x():
     """dz = NULL keeps dz in the workspace; dx may overwrite x in place."""
     g = Geometry(2, 12, 12, 32, 32, 3, 3, 1, 1)

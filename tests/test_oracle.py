@@ -80,6 +80,24 @@ def test_conv_matches_torch_conv2d(g):
     np.testing.assert_allclose(z, zt, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("g", [GEOMS[0], GEOMS[3]] + ANISO[:1], ids=str)
+def test_conv_bias_act_matches_brute_force(g):
+    """Conv2D + bias (+ ReLU) without batch normalisation: the brute-force loop nest plus
+    the bias, then max(., 0); a NULL bias adds nothing."""
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((g.n, g.h, g.w, g.c))
+    w = rng.standard_normal((g.k, g.r, g.s, g.c))
+    b = rng.standard_normal(g.k)
+    ref = brute_conv(x, w, g.sh, g.sw, g.ph, g.pw)
+    assert (ref + b < 0).any() and (ref + b > 0).any()
+    sp = oshape(g)
+    np.testing.assert_allclose(oracle.conv2d_bias_act(sp, x, w, b, relu=False), ref + b, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.conv2d_bias_act(sp, x, w, b, relu=True), np.maximum(ref + b, 0.0),
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.conv2d_bias_act(sp, x, w, None, relu=True), np.maximum(ref, 0.0),
+                               rtol=1e-13, atol=1e-13)
+
+
 def test_conv_1x1_is_matmul():
     g = Geometry(3, 5, 7, 6, 4, 1, 1, 1, 0)
     rng = np.random.default_rng(13)
