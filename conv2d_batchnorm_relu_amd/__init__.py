@@ -18,7 +18,7 @@ import os
 
 __all__ = ["CbrError", "CbrShape", "make_shape", "cbr_status_str", "cbr_output_hw", "cbr_mask_words",
            "cbr_workspace_bytes", "cbr_forward_train", "cbr_forward_infer", "cbr_backward",
-           "cbr_conv2d_bias_relu", "cbr_conv2d_bias",
+           "cbr_conv2d_bias_relu", "cbr_conv2d_bias", "cbr_forward_train_noalloc",
            "CBR_OP_TRAIN", "CBR_OP_INFER", "CBR_OP_BWD", "library_path"]
 
 CBR_OP_TRAIN, CBR_OP_INFER, CBR_OP_BWD = 0, 1, 2
@@ -76,6 +76,9 @@ def _load():
     lib.cbr_forward_infer_ev.restype = ctypes.c_int
     lib.cbr_backward_ev.argtypes = lib.cbr_backward.argtypes + [P]
     lib.cbr_backward_ev.restype = ctypes.c_int
+    lib.cbr_forward_train_noalloc.argtypes = [S, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                              P, P, P, P, P, P, P, P]
+    lib.cbr_forward_train_noalloc.restype = ctypes.c_int
     for name in ("cbr_conv2d_bias_relu", "cbr_conv2d_bias"):
         fn, fe = getattr(lib, name), getattr(lib, name + "_ev")
         fn.argtypes = [S, P, P, P, P, P]
@@ -180,6 +183,17 @@ def cbr_forward_train(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, mo
         _check(_load().cbr_forward_train(*args), f)
     else:
         _check(_load().cbr_forward_train_ev(*args, _events(events)), "cbr_forward_train_ev")
+
+
+def cbr_forward_train_noalloc(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, momentum,
+                              z, y, relu_mask, saved_mean, saved_invstd, run_mean_out, run_var_out, stream=None):
+    f = "cbr_forward_train_noalloc"
+    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(gamma, 4, "gamma", f),
+            _ptr(beta, 4, "beta", f), _ptr(run_mean_in, 4, "run_mean_in", f), _ptr(run_var_in, 4, "run_var_in", f),
+            float(eps), float(momentum), _ptr(z, 2, "z", f), _ptr(y, 2, "y", f), _ptr(relu_mask, 4, "relu_mask", f),
+            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f),
+            _ptr(run_mean_out, 4, "run_mean_out", f), _ptr(run_var_out, 4, "run_var_out", f), _stream(stream))
+    _check(_load().cbr_forward_train_noalloc(*args), f)
 
 
 def cbr_forward_infer(shape, x, w, conv_bias, gamma, beta, run_mean, run_var, eps, y,

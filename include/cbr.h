@@ -153,6 +153,31 @@ int cbr_backward(const cbr_shape *shape,
                  void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The training forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments
+ * and results as cbr_forward_train without the workspace: the kernels' scratch is a
+ * CBR_NOALLOC_SCRATCH_BYTES array that the library holds on each device from the first
+ * call made with that device current until the process ends (its address is looked up
+ * then, with hipGetSymbolAddress).  The call itself allocates nothing.
+ * Limit: shapes whose cbr_workspace_bytes(shape, CBR_OP_TRAIN) exceeds
+ * CBR_NOALLOC_SCRATCH_BYTES return CBR_E_WORKSPACE (the 256 x 56 x 56 x 64 workload needs
+ * about 140 KB, the 224 x 224 first layer at N = 64 about 1 MB).
+ * All calls on one device share that device's array: calls that may overlap on one
+ * device (different streams, different host threads) race, and must be serialised by
+ * the caller.  A call leaves the array's contents undefined; no call depends on them.
+ */
+#define CBR_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+int cbr_forward_train_noalloc(const cbr_shape *shape,
+                              const uint16_t *x, const uint16_t *w,
+                              const float *gamma, const float *beta,
+                              const float *run_mean_in, const float *run_var_in,
+                              float eps, float momentum,
+                              uint16_t *z, uint16_t *y, uint32_t *relu_mask,
+                              float *saved_mean, float *saved_invstd,
+                              float *run_mean_out, float *run_var_out, void *stream);
+
+/*
  * Conv2D + bias + ReLU without batch normalisation ([TL] "fused ReLU" section: the ReLU
  * applied in the convolution's epilogue, before the result leaves the chip):
  *   y = max(conv(x, w) + bias, 0)                                  bf16 [N,P,Q,K] (out)

@@ -191,3 +191,14 @@ def test_binding_rejects_unusable_tensors():
         cbr.cbr_forward_infer(sp, host, host, None, host, host, host, host, 1e-5, host, None)
     with pytest.raises(cbr.CbrError, match="not a GPU tensor"):
         cbr.cbr_backward(sp, host, host, host, host, host, host, host, host, None, host, host, host, None, None)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The allocation-free training forward refuses, before touching the GPU, a shape whose
+    scratch needs exceed its fixed array; shape errors keep their own codes."""
+    big = cbr.make_shape(4096, 56, 56, 64, 72, 3, 3, 1, 1)   # generic conv: ~100k statistics rows
+    assert cbr.cbr_workspace_bytes(big, cbr.CBR_OP_TRAIN) > 4 << 20
+    fn = cbr._load().cbr_forward_train_noalloc
+    assert fn(ctypes.byref(big), *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 5      # CBR_E_WORKSPACE
+    assert fn(ctypes.byref(shp(k=12)), *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 3
+    assert fn(None, *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 1
