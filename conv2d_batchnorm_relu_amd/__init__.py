@@ -52,6 +52,10 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
                           "(the CBR operator has no CPU fallback)")
+    # The library must resolve its HIP runtime to the one that owns the callers' device
+    # memory and streams.  torch loads its own copy of the runtime; loading torch first
+    # makes the library bind to that copy (same soname) instead of a second one.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     S = ctypes.POINTER(CbrShape)

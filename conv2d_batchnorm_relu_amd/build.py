@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcbr.so")
 SOURCES = ["conv_fprop.hip", "conv_igemm.hip", "conv3x3_c64.hip", "conv_c3s2.hip", "bn_fwd.hip", "bn_bwd.hip",
-           "conv_wgrad.hip", "cbr_api.cpp", "cbr_noalloc.hip"]
+           "conv_wgrad.hip", "cbr_api.cpp", "cbr_plan.cpp", "cbr_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for device code (hipcc's host pass warns that

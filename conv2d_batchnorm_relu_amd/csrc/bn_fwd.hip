@@ -111,12 +111,15 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
 
 }  // namespace
 
-int train_partial_rows(const ConvGeom &g)
+int train_partial_rows(const ConvGeom &g, int plan)
 {
-    return halo_eligible(g)                ? halo_grid(g)
-           : c3s2_eligible(g)              ? c3s2_grid(g)
-           : igemm_eligible(g, EPI_STATS) ? igemm_partial_rows(g)
-                                           : conv_plan(g).tiles_m;
+    switch (plan) {
+    case PLAN_PERSIST3X3: return halo_grid(g);
+    case PLAN_FIRST_LAYER: return c3s2_grid(g);
+    case PLAN_IG_224X256:
+    case PLAN_IG_448X128: return igemm_partial_rows(g, plan);
+    default: return conv_plan(g, plan).tiles_m;
+    }
 }
 
 hipError_t launch_stats_finalize(int rows, int K, const float *partials, const BnFinalizeArgs &fin, hipStream_t st,

@@ -42,8 +42,10 @@ int make_geom(const cbr_shape *s, ConvGeom *g)
     return CBR_OK;
 }
 
+}  // namespace
+
 // The data gradient as a stride-1 forward convolution of dz with the flipped filter.
-ConvGeom dgrad_geom(const ConvGeom &g)
+ConvGeom cbr::dgrad_geom(const ConvGeom &g)
 {
     ConvGeom d;
     d.N = g.N; d.H = g.P; d.W = g.Q; d.C = g.K;
@@ -55,18 +57,20 @@ ConvGeom dgrad_geom(const ConvGeom &g)
     return d;
 }
 
+namespace {
+
 struct TrainLayout { size_t partials, scale, shift, wexp, total; };
 struct InferLayout { size_t wfold, bfold, total; };
 struct BwdLayout { size_t dz, part, coef, wpart, wflip, total; };
 
-TrainLayout train_layout(const ConvGeom &g)
+TrainLayout train_layout(const ConvGeom &g, int plan)
 {
     TrainLayout L;
     size_t o = 0;
-    L.partials = o; o = align_up(o + sizeof(float) * (2 * g.K + 1) * (size_t)train_partial_rows(g));
+    L.partials = o; o = align_up(o + sizeof(float) * (2 * g.K + 1) * (size_t)train_partial_rows(g, plan));
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
-    L.wexp = o; o = align_up(o + (c3s2_eligible(g) ? c3s2_wexp_bytes(g) : 0));
+    L.wexp = o; o = align_up(o + (plan == PLAN_FIRST_LAYER ? c3s2_wexp_bytes(g) : 0));
     L.total = o;
     return L;
 }
@@ -81,10 +85,10 @@ InferLayout infer_layout(const ConvGeom &g)
     return L;
 }
 
-BwdLayout bwd_layout(const ConvGeom &g)
+BwdLayout bwd_layout(const ConvGeom &g, int wplan)
 {
     BwdLayout L;
-    const WgradPlan wp = wgrad_plan(g);
+    const WgradPlan wp = wgrad_plan(g, wplan);
     size_t o = 0;
     L.dz = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.M * g.K);
     L.part = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)bnbwd_blocks(g.M, g.K));
@@ -149,9 +153,9 @@ size_t cbr_workspace_bytes(const cbr_shape *shape, int op)
     ConvGeom g;
     if (make_geom(shape, &g) != CBR_OK) return 0;
     switch (op) {
-    case CBR_OP_TRAIN: return train_layout(g).total;
+    case CBR_OP_TRAIN: return train_layout(g, resolve_plan(g, STAGE_TRAIN)).total;
     case CBR_OP_INFER: return infer_layout(g).total;
-    case CBR_OP_BWD: return bwd_layout(g).total;
+    case CBR_OP_BWD: return bwd_layout(g, resolve_plan(g, STAGE_WGRAD)).total;
     default: return 0;
     }
 }
@@ -173,7 +177,8 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
         return CBR_E_ALIGN;
     if (g.M < 2) return CBR_E_SHAPE;   // batch statistics need two values per channel
     if (!(eps >= 0.f) || !isfinite(eps) || !(momentum >= 0.f && momentum <= 1.f)) return CBR_E_VALUE;
-    const TrainLayout L = train_layout(g);
+    const int plan = resolve_plan(g, STAGE_TRAIN);
+    const TrainLayout L = train_layout(g, plan);
     if (!workspace || ws_bytes < L.total) return CBR_E_WORKSPACE;
     if (!aligned16(workspace)) return CBR_E_ALIGN;
 
@@ -185,13 +190,14 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
                              scale, shift, saved_mean,  saved_invstd, run_mean_out, run_var_out};
     // conv + channel sums (CBR page 4.1) -> finalize (4.2) -> apply + ReLU + mask (4.3)
     const hipError_t ec =
-        halo_eligible(g)   ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
-        : c3s2_eligible(g) ? launch_conv_c3s2_stats(g, x, w, (uint16_t *)ws_at(workspace, L.wexp), z, partials, s,
-                                                    ev(events, 0), ev(events, 1))
-                           : launch_conv_fprop(g, EPI_STATS, x, w, nullptr, z, partials, s, ev(events, 0),
-                                               ev(events, 1));
+        plan == PLAN_PERSIST3X3
+            ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
+        : plan == PLAN_FIRST_LAYER
+            ? launch_conv_c3s2_stats(g, x, w, (uint16_t *)ws_at(workspace, L.wexp), z, partials, s, ev(events, 0),
+                                     ev(events, 1))
+            : launch_conv_fprop(g, EPI_STATS, plan, x, w, nullptr, z, partials, s, ev(events, 0), ev(events, 1));
     if (ec != hipSuccess) return CBR_E_HIP;
-    if (launch_stats_finalize(train_partial_rows(g), g.K, partials, fin, s, ev(events, 2), ev(events, 3)) !=
+    if (launch_stats_finalize(train_partial_rows(g, plan), g.K, partials, fin, s, ev(events, 2), ev(events, 3)) !=
         hipSuccess)
         return CBR_E_HIP;
     if (launch_bn_apply_relu_mask(g.M, g.K, z, scale, shift, y, (uint8_t *)relu_mask, s, ev(events, 4),
@@ -233,7 +239,8 @@ int cbr_forward_infer_ev(const cbr_shape *shape, const uint16_t *x, const uint16
     if (launch_bn_fold(g.K, g.Kg, w, conv_bias, gamma, beta, run_mean, run_var, eps, wf, bf, s, ev(events, 0),
                        ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    if (launch_conv_fprop(g, EPI_BIAS_RELU, x, wf, bf, y, nullptr, s, ev(events, 2), ev(events, 3)) != hipSuccess)
+    if (launch_conv_fprop(g, EPI_BIAS_RELU, resolve_plan(g, STAGE_INFER), x, wf, bf, y, nullptr, s, ev(events, 2),
+                          ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
     return CBR_OK;
 }
@@ -256,8 +263,8 @@ static int conv_bias_act(const cbr_shape *shape, const uint16_t *x, const uint16
     if (st != CBR_OK) return st;
     if (any_null(x, w, y)) return CBR_E_NULL;
     if (!all_aligned(x, w, y) || (bias && !aligned16(bias))) return CBR_E_ALIGN;
-    if (launch_conv_fprop(g, relu ? EPI_BIAS_RELU : EPI_BIAS, x, w, bias, y, nullptr, (hipStream_t)stream,
-                          ev(events, 0), ev(events, 1)) != hipSuccess)
+    if (launch_conv_fprop(g, relu ? EPI_BIAS_RELU : EPI_BIAS, resolve_plan(g, STAGE_INFER), x, w, bias, y, nullptr,
+                          (hipStream_t)stream, ev(events, 0), ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
     return CBR_OK;
 }
@@ -300,7 +307,8 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
         return CBR_E_ALIGN;
     if (g.M < 2) return CBR_E_SHAPE;
     if (dx && (g.sh != 1 || g.sw != 1)) return CBR_E_UNSUPPORTED;
-    const BwdLayout L = bwd_layout(g);
+    const int wplan = resolve_plan(g, STAGE_WGRAD);
+    const BwdLayout L = bwd_layout(g, wplan);
     if (!workspace || ws_bytes < L.total) return CBR_E_WORKSPACE;
     if (!aligned16(workspace)) return CBR_E_ALIGN;
 
@@ -314,14 +322,15 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
                            (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s, ev(events, 0),
                            ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    if (launch_conv_wgrad(g, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s, ev(events, 2), ev(events, 3)) !=
-        hipSuccess)
+    if (launch_conv_wgrad(g, wplan, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s, ev(events, 2),
+                          ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
     if (dx) {
         uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
         if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, ev(events, 4), nullptr) != hipSuccess) return CBR_E_HIP;
         const ConvGeom d = dgrad_geom(g);
-        if (launch_conv_fprop(d, EPI_PLAIN, dzp, wt, nullptr, dx, nullptr, s, nullptr, ev(events, 5)) != hipSuccess)
+        if (launch_conv_fprop(d, EPI_PLAIN, resolve_plan(g, STAGE_DGRAD), dzp, wt, nullptr, dx, nullptr, s, nullptr,
+                              ev(events, 5)) != hipSuccess)
             return CBR_E_HIP;
     } else if (events && (hipEventRecord(ev(events, 4), s) != hipSuccess ||
                           hipEventRecord(ev(events, 5), s) != hipSuccess)) {
@@ -338,5 +347,27 @@ int cbr_backward(const cbr_shape *shape, const uint16_t *x, const uint16_t *w, c
     return cbr_backward_ev(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd, dz, dgamma, dbeta, dw,
                            dx, workspace, ws_bytes, stream, nullptr);
 }
+
+int cbr_plan_of(const cbr_shape *shape, int stage)
+{
+    ConvGeom g;
+    const int st = make_geom(shape, &g);
+    if (st != CBR_OK) return -st;
+    if (stage < 0 || stage >= NSTAGES) return -CBR_E_VALUE;
+    return resolve_plan(g, stage);
+}
+
+int cbr_plan_eligible(const cbr_shape *shape, int stage, int plan)
+{
+    ConvGeom g;
+    const int st = make_geom(shape, &g);
+    if (st != CBR_OK) return -st;
+    if (stage < 0 || stage >= NSTAGES) return -CBR_E_VALUE;
+    return plan_eligible(g, stage, plan) ? 1 : 0;
+}
+
+const char *cbr_plan_name(int plan) { return plan_name(plan); }
+
+int cbr_set_plan_override(int stage, int plan) { return set_plan_override(stage, plan) ? CBR_OK : CBR_E_VALUE; }
 
 }  // extern "C"

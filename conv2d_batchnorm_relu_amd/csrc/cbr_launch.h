@@ -43,15 +43,43 @@ inline hipError_t launch(Kern k, dim3 grid, dim3 block, uint32_t shmem, hipStrea
     return hipGetLastError();
 }
 
-// Tile plan of the implicit-GEMM convolution: BM output pixels x BN output channels
-// per workgroup.  The plan is a pure function of the geometry, so workspace sizing and
-// launches always agree.
+// Kernel plans.  Each convolution stage of a call -- the training forward's conv, the
+// inference / conv + bias conv, the data gradient's conv and the weight gradient -- runs
+// one of these kernels and tile shapes.  resolve_plan picks it per geometry: a tuning
+// override if one is set, else the compiled-in table the offline tuner writes, else the
+// default rule; every path returns a plan that is eligible for the geometry.  The choice
+// is a pure function of (geometry, stage, override), so workspace sizing and launches
+// agree.
+enum Stage { STAGE_TRAIN = 0, STAGE_INFER = 1, STAGE_DGRAD = 2, STAGE_WGRAD = 3, NSTAGES = 4 };
+enum Plan {
+    PLAN_DEFAULT = 0,
+    PLAN_PERSIST3X3 = 1,    // persistent 3x3 / 64-channel conv + statistics (training only)
+    PLAN_FIRST_LAYER = 2,   // 3-channel stride-2 first-layer conv + statistics (training only)
+    PLAN_IG_224X256 = 3,    // persistent large-tile conv, 224 x 256 chunks (K % 256 == 0)
+    PLAN_IG_448X128 = 4,    // persistent large-tile conv, 448 x 128 chunks (K % 128 == 0)
+    PLAN_GEN_128X128 = 5,   // generic implicit-GEMM conv, 128 x 128 tiles
+    PLAN_GEN_128X64 = 6,    // generic implicit-GEMM conv, 128 x 64 tiles
+    PLAN_WG_TR = 7,         // weight gradient with transposed LDS reads (C % 128, K % 256)
+    PLAN_WG_GEN = 8,        // generic weight gradient
+    NPLANS = 9
+};
+// g is always the layer's geometry (cbr_shape); for STAGE_DGRAD the plan runs, and is
+// checked on, the data gradient's convolution dgrad_geom(g).
+bool plan_eligible(const ConvGeom &g, int stage, int plan);
+int resolve_plan(const ConvGeom &g, int stage);
+int default_plan(const ConvGeom &g, int stage);
+ConvGeom dgrad_geom(const ConvGeom &g);
+const char *plan_name(int plan);
+bool set_plan_override(int stage, int plan);
+
+// Tile plan of the generic implicit-GEMM convolution: BM output pixels x BN output
+// channels per workgroup.
 struct ConvPlan {
     int bm, bn;
     bool vec;     // input channels a multiple of 8: 16-byte gathers
     int tiles_m, tiles_n;
 };
-ConvPlan conv_plan(const ConvGeom &g);
+ConvPlan conv_plan(const ConvGeom &g, int plan);
 
 // Persistent 3x3 / stride 1 / pad 1, 64 -> 64 channel convolution + channel statistics.
 constexpr int HALO_MAX_GRID = 256;                        // one workgroup per MI355X CU
@@ -75,7 +103,7 @@ hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const ui
 // area holds R rows of [2][K] fp32 (each channel's mean over the row's output pixels,
 // then its M2 = sum of squared deviations from that mean), followed by R fp32 pixel
 // counts; a row with count 0 holds zeros.
-int train_partial_rows(const ConvGeom &g);
+int train_partial_rows(const ConvGeom &g, int plan);
 
 // Blocks of the BN-backward reduction over M rows of K channels.
 int bnbwd_blocks(int M, int K);
@@ -87,17 +115,21 @@ struct WgradPlan {
     int tiles_m, tiles_n, splits;
     int rows_per_split;   // output pixels per split (multiple of the pixel step)
 };
-WgradPlan wgrad_plan(const ConvGeom &g);
+bool wgrad_tr_eligible(const ConvGeom &g);
+WgradPlan wgrad_plan(const ConvGeom &g, int plan);
 
-// Persistent large-tile implicit-GEMM conv (C % 32 == 0, K a multiple of 128): at most
-// 256 workgroups, each over a contiguous range of output pixels; with EPI_STATS one
-// partial row per workgroup.  launch_conv_fprop takes it whenever it is eligible.
-bool igemm_eligible(const ConvGeom &g, int epi);
-int igemm_partial_rows(const ConvGeom &g);
-hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w, const float *bias,
-                             uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+// Persistent large-tile implicit-GEMM conv (C % 32 == 0, K a multiple of the chunk's
+// channels): at most 256 workgroups, each over a contiguous range of output pixels; with
+// EPI_STATS one partial row per pixel chunk.  plan: PLAN_IG_224X256 or PLAN_IG_448X128.
+bool igemm_eligible(const ConvGeom &g, int epi, int plan);
+int igemm_partial_rows(const ConvGeom &g, int plan);
+hipError_t launch_conv_igemm(const ConvGeom &g, int epi, int plan, const uint16_t *x, const uint16_t *w,
+                             const float *bias, uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0,
+                             hipEvent_t e1);
 
-hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w,
+// A forward convolution with epilogue epi on the large-tile or the generic kernel, as
+// plan says (PLAN_IG_* or PLAN_GEN_*).
+hipError_t launch_conv_fprop(const ConvGeom &g, int epi, int plan, const uint16_t *x, const uint16_t *w,
                              const float *bias, uint16_t *out, float *partials, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
@@ -122,7 +154,7 @@ hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *
 hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt,
                                hipStream_t st, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16_t *x,
+hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, const uint16_t *x,
                              float *part, float *dw, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 

@@ -351,23 +351,24 @@ hipError_t launch_mode(const ConvGeom &g, int epi, const ConvParams &prm, dim3 g
 
 }  // namespace
 
-ConvPlan conv_plan(const ConvGeom &g)
+ConvPlan conv_plan(const ConvGeom &g, int plan)
 {
     ConvPlan p;
     p.bm = 128;
-    p.bn = (g.K >= 128) ? 128 : 64;
+    p.bn = plan == PLAN_GEN_128X64 ? 64 : 128;
     p.vec = (g.C % 8) == 0;
     p.tiles_m = (g.M + p.bm - 1) / p.bm;
     p.tiles_n = (g.K + p.bn - 1) / p.bn;
     return p;
 }
 
-hipError_t launch_conv_fprop(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w,
+hipError_t launch_conv_fprop(const ConvGeom &g, int epi, int plan, const uint16_t *x, const uint16_t *w,
                              const float *bias, uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0,
                              hipEvent_t e1)
 {
-    if (igemm_eligible(g, epi)) return launch_conv_igemm(g, epi, x, w, bias, out, partials, st, e0, e1);
-    const ConvPlan p = conv_plan(g);
+    if (plan == PLAN_IG_224X256 || plan == PLAN_IG_448X128)
+        return launch_conv_igemm(g, epi, plan, x, w, bias, out, partials, st, e0, e1);
+    const ConvPlan p = conv_plan(g, plan);
     ConvParams prm{g, x, w, bias, out, partials};
     dim3 grid(p.tiles_m, p.tiles_n);
     if (p.bn == 128) return launch_mode<128, 128>(g, epi, prm, grid, st, e0, e1);

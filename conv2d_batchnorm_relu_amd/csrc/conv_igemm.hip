@@ -509,21 +509,21 @@ struct IgConfig {
 int ig_grid(const ConvGeom &g) { return std::min(256, (g.M + 31) / 32); }
 int ig_rows_per_wg(const ConvGeom &g) { return (g.M + ig_grid(g) - 1) / ig_grid(g); }
 
-// K = 256 with at most 224 pixels per workgroup: one 224 x 256 chunk per workgroup, eight
-// waves side by side over the channels (two per SIMD).  Otherwise chunks of 448 pixels x
-// 128 channels, eight waves in a 2 x 4 grid of 224 x 32 wave tiles.  Slices of 64
-// reduction elements (whole 128-byte rows) when C % 64 == 0, two in flight; else of 32,
-// four in flight.  The epilogue stages in the slice buffers.
-IgConfig ig_config(const ConvGeom &g)
+// PLAN_IG_224X256: chunks of 224 pixels x 256 channels, eight waves side by side over the
+// channels (two per SIMD).  PLAN_IG_448X128: chunks of 448 pixels x 128 channels, eight
+// waves in a 2 x 4 grid of 224 x 32 wave tiles.  Slices of 64 reduction elements (whole
+// 128-byte rows) when C % 64 == 0, two in flight; else of 32, four in flight.  The
+// epilogue stages in the slice buffers.
+IgConfig ig_config(const ConvGeom &g, int plan)
 {
     const bool wide = g.C % 64 == 0;
-    if (g.K == 256 && ig_rows_per_wg(g) <= 224) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4};
+    if (plan == PLAN_IG_224X256) return IgConfig{7, 1, 1, 8, wide ? 64 : 32, wide ? 2 : 4};
     return IgConfig{7, 1, 2, 4, wide ? 64 : 32, wide ? 2 : 4};
 }
 
-size_t ig_lds_bytes(const ConvGeom &g, int epi)
+size_t ig_lds_bytes(const ConvGeom &g, int epi, int plan)
 {
-    const IgConfig c = ig_config(g);
+    const IgConfig c = ig_config(g, plan);
     const size_t stage = (size_t)c.nstage * (c.bm() + c.bn()) * 2 * c.bk;
     const size_t scr = epi == EPI_STATS ? (size_t)c.nw() * 64 * c.nj * 32 * 4 : 0;
     const size_t stg = std::max((size_t)c.bm() * 2 * c.bn(), scr);
@@ -557,24 +557,29 @@ hipError_t ig_launch_cfg(int epi, const IgParams &prm, int grid, size_t lds, hip
 
 }  // namespace
 
-bool igemm_eligible(const ConvGeom &g, int epi)
+bool igemm_eligible(const ConvGeom &g, int epi, int plan)
 {
+    if (plan != PLAN_IG_224X256 && plan != PLAN_IG_448X128) return false;
     if (g.C % 32 != 0 || g.M <= 0 || g.R > 16 || g.S > 16) return false;
-    const IgConfig c = ig_config(g);
+    const IgConfig c = ig_config(g, plan);
     if (g.K % c.bn() != 0) return false;
     const double xbytes = 2.0 * g.N * g.H * g.W * g.C, obytes = 2.0 * g.M * g.K, wbytes = 2.0 * g.K * g.Kg;
     if (xbytes >= 2147483648.0 || obytes >= 2147483648.0 || wbytes >= 2147483648.0) return false;
-    return ig_lds_bytes(g, epi) <= 160 * 1024;
+    return ig_lds_bytes(g, epi, plan) <= 160 * 1024;
 }
 
-int ig_maxmc(const ConvGeom &g) { return (ig_rows_per_wg(g) + ig_config(g).bm() - 1) / ig_config(g).bm(); }
-
-int igemm_partial_rows(const ConvGeom &g) { return ig_grid(g) * ig_maxmc(g); }
-
-hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, const uint16_t *w, const float *bias,
-                             uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+int ig_maxmc(const ConvGeom &g, int plan)
 {
-    const IgConfig c = ig_config(g);
+    return (ig_rows_per_wg(g) + ig_config(g, plan).bm() - 1) / ig_config(g, plan).bm();
+}
+
+int igemm_partial_rows(const ConvGeom &g, int plan) { return ig_grid(g) * ig_maxmc(g, plan); }
+
+hipError_t launch_conv_igemm(const ConvGeom &g, int epi, int plan, const uint16_t *x, const uint16_t *w,
+                             const float *bias, uint16_t *out, float *partials, hipStream_t st, hipEvent_t e0,
+                             hipEvent_t e1)
+{
+    const IgConfig c = ig_config(g, plan);
     IgParams prm;
     prm.x = x;
     prm.w = w;
@@ -589,9 +594,9 @@ hipError_t launch_conv_igemm(const ConvGeom &g, int epi, const uint16_t *x, cons
     prm.ksteps = g.Kg / c.bk;
     prm.rows_per_wg = ig_rows_per_wg(g);
     prm.ntn = g.K / c.bn();
-    prm.maxmc = ig_maxmc(g);
+    prm.maxmc = ig_maxmc(g, plan);
     const int grid = ig_grid(g);
-    const size_t lds = ig_lds_bytes(g, epi);
+    const size_t lds = ig_lds_bytes(g, epi, plan);
     if (c.wgm == 1) {
         if (c.bk == 64) return ig_launch_cfg<7, 1, 1, 8, 64, 2>(epi, prm, grid, lds, st, e0, e1);
         return ig_launch_cfg<7, 1, 1, 8, 32, 4>(epi, prm, grid, lds, st, e0, e1);

@@ -562,19 +562,19 @@ __global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
             }
 }
 
+}  // namespace
+
 bool wgrad_tr_eligible(const ConvGeom &g)
 {
     const double xbytes = 2.0 * g.N * g.H * g.W * g.C, zbytes = 2.0 * g.M * g.K;
     return g.C % TR_BN == 0 && g.K % TR_BM == 0 && g.M > 0 && xbytes < 2147483648.0 && zbytes < 2147483648.0;
 }
 
-}  // namespace
-
-WgradPlan wgrad_plan(const ConvGeom &g)
+WgradPlan wgrad_plan(const ConvGeom &g, int plan)
 {
     const int M = g.M, K = g.K, Kg = g.Kg;
     WgradPlan p;
-    p.tr = wgrad_tr_eligible(g);
+    p.tr = plan == PLAN_WG_TR;
     if (p.tr) {
         // one workgroup per CU: 256 x 128 tiles, the pixel range split to fill the rest
         p.bm = TR_BM;
@@ -603,10 +603,10 @@ WgradPlan wgrad_plan(const ConvGeom &g)
     return p;
 }
 
-hipError_t launch_conv_wgrad(const ConvGeom &g, const uint16_t *dz, const uint16_t *x, float *part, float *dw,
-                             hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, const uint16_t *x, float *part,
+                             float *dw, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const WgradPlan p = wgrad_plan(g);
+    const WgradPlan p = wgrad_plan(g, plan);
     if (p.tr) {
         WgradTrParams tp;
         tp.dz = dz;

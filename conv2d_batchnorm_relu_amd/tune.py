@@ -1,0 +1,185 @@
+"""Offline tuner of the per-shape kernel plans (the MI355X counterpart of the CBR page's
+empirical engine search, section 7, and of the TileLang page's autotuned tile
+configurations).
+
+For every layer shape of a list (the conv layers of ResNet-50 and VGG16-BN at the given
+batch sizes) and every stage of a call -- the training forward's conv, the inference
+conv, the data gradient, the weight gradient -- it times each plan the library reports
+eligible (cbr_plan_eligible), forcing it with cbr_set_plan_override, and keeps the
+fastest.  It writes the table that csrc/cbr_plan.cpp compiles in (cbr_tune_table.inc)
+and a markdown summary of every timing.  Rebuild the library after replacing the table.
+
+    python -m conv2d_batchnorm_relu_amd.tune --out-dir gpurun_out/tune [--batch 32 256] [--reps 15]
+
+Timings are HIP events on the kernels' own dispatch packets (the _ev calls), median of
+--reps calls after a warm-up, on synthetic N(0,1) inputs (values do not change the
+kernels' work).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import statistics
+import sys
+import time
+
+STAGES = {0: "train_conv", 1: "infer_conv", 2: "dgrad", 3: "wgrad"}
+PLANS = range(1, 9)
+
+
+def resnet50_layers():
+    """(H, W, C, K, R, S, stride, pad) of ResNet-50's conv layers (v1.5: stride on the 3x3)."""
+    L = [(224, 224, 3, 64, 7, 7, 2, 3)]
+    for hw, cin, mid, out, first_stride in ((56, 64, 64, 256, 1), (56, 256, 128, 512, 2),
+                                             (28, 512, 256, 1024, 2), (14, 1024, 512, 2048, 2)):
+        ohw = hw // first_stride
+        L += [(hw, hw, cin, mid, 1, 1, 1, 0),                  # first block's 1x1 reduce
+              (hw, hw, mid, mid, 3, 3, first_stride, 1),       # first block's 3x3
+              (ohw, ohw, mid, out, 1, 1, 1, 0),                # 1x1 expand
+              (hw, hw, cin, out, 1, 1, first_stride, 0),       # projection shortcut
+              (ohw, ohw, out, mid, 1, 1, 1, 0),                # later blocks' 1x1 reduce
+              (ohw, ohw, mid, mid, 3, 3, 1, 1)]                # later blocks' 3x3
+    return sorted(set(L), key=L.index)
+
+
+def vgg16_layers():
+    L = []
+    for hw, cin, cout, n in ((224, 3, 64, 1), (224, 64, 64, 1), (112, 64, 128, 1), (112, 128, 128, 1),
+                             (56, 128, 256, 1), (56, 256, 256, 1), (28, 256, 512, 1), (28, 512, 512, 1),
+                             (14, 512, 512, 1)):
+        L.append((hw, hw, cin, cout, 3, 3, 1, 1))
+    return L
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--out-dir", default="gpurun_out/tune")
+    ap.add_argument("--batch", type=int, nargs="+", default=[32, 256])
+    ap.add_argument("--vgg-batch", type=int, nargs="+", default=[32])
+    ap.add_argument("--reps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--max-elems", type=int, default=1 << 29, help="skip layers whose tensors exceed this")
+    args = ap.parse_args(argv)
+
+    import torch
+    import conv2d_batchnorm_relu_amd as cbr
+
+    lib = cbr._load()
+    lib.cbr_plan_name.restype = ctypes.c_char_p
+    dev = torch.device("cuda:0")
+    os.makedirs(args.out_dir, exist_ok=True)
+
+    def log(msg):
+        print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+    def events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    layers = [("resnet50", n, L) for n in args.batch for L in resnet50_layers()]
+    layers += [("vgg16bn", n, L) for n in args.vgg_batch for L in vgg16_layers()]
+    entries, report = [], []
+    for net, n, (h, w, c, k, r, s, st, pd) in layers:
+        sp = cbr.make_shape(n, h, w, c, k, r, s, st, pd)
+        try:
+            P, Q = cbr.cbr_output_hw(sp)
+        except cbr.CbrError as e:
+            log(f"skip {net} {n}x{h}x{w}x{c}->{k} {r}x{s}/{st}: {e}")
+            continue
+        if max(n * h * w * c, n * P * Q * k) > args.max_elems:
+            log(f"skip {net} {n}x{h}x{w}x{c}->{k}: larger than --max-elems")
+            continue
+        x = torch.randn(n, h, w, c, device=dev).to(torch.bfloat16)
+        wt = (torch.rand(k, r, s, c, device=dev) - 0.5).to(torch.bfloat16)
+        vk = [torch.rand(k, device=dev) + 0.5 for _ in range(6)]
+        z = torch.empty(n, P, Q, k, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(z)
+        mask = torch.empty(cbr.cbr_mask_words(sp), dtype=torch.int32, device=dev)
+        dy = torch.randn(n, P, Q, k, device=dev).to(torch.bfloat16)
+        dz = torch.empty_like(z)
+        dwt = torch.empty(k, r, s, c, device=dev)
+        dx = torch.empty_like(x) if st == 1 else None
+
+        def run_train(ev):
+            ws = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_TRAIN)), dtype=torch.uint8, device=dev)
+            cbr.cbr_forward_train(sp, x, wt, vk[0], vk[1], vk[2], vk[3], 1e-5, 0.1, z, y, mask, vk[4], vk[5],
+                                  vk[2], vk[3], ws, events=ev)
+            return ws
+
+        def run_infer(ev):
+            cbr.cbr_conv2d_bias_relu(sp, x, wt, vk[0], y, events=ev)
+
+        def run_bwd(ev):
+            ws = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_BWD)), dtype=torch.uint8, device=dev)
+            cbr.cbr_backward(sp, x, wt, z, mask, dy, vk[0], vk[4], vk[5], dz, vk[1], vk[2], dwt, dx, ws, events=ev)
+            return ws
+
+        run_train(None)   # a z, mask and saved statistics for the backward
+        torch.cuda.synchronize()
+        for stage, sname in STAGES.items():
+            if stage == 2 and st != 1:
+                continue   # the data gradient needs stride 1
+            cands = [p for p in PLANS if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
+            default = lib.cbr_plan_of(ctypes.byref(sp), stage)
+            times = {}
+            for plan in cands:
+                lib.cbr_set_plan_override(stage, plan)
+                fn, nev, pair = ((run_train, 6, None) if stage == 0 else (run_infer, 2, (0, 1)) if stage == 1
+                                 else (run_bwd, 6, (4, 5) if stage == 2 else (2, 3)))
+                try:
+                    for _ in range(args.warmup):
+                        fn(None)
+                    torch.cuda.synchronize()
+                    ts = []
+                    for _ in range(args.reps):
+                        ev = events(nev)
+                        keep = fn(ev)
+                        torch.cuda.synchronize()
+                        if pair is None:
+                            ts.append(ev[0].elapsed_time(ev[5]) * 1000.0)
+                        else:
+                            ts.append(ev[pair[0]].elapsed_time(ev[pair[1]]) * 1000.0)
+                        del keep
+                    times[plan] = statistics.median(ts)
+                finally:
+                    lib.cbr_set_plan_override(stage, 0)
+            if not times:
+                continue
+            best = min(times, key=times.get)
+            name = lambda p: lib.cbr_plan_name(p).decode()
+            log(f"{net} N{n} {h}x{w} {c}->{k} {r}x{s}/{st} {sname}: " +
+                ", ".join(f"{name(p)} {t:.1f}us" for p, t in sorted(times.items(), key=lambda kv: kv[1])) +
+                f" (default {name(default)})")
+            report.append((net, n, h, w, c, k, r, s, st, pd, sname, times, best, default))
+            if len(times) > 1:
+                runner = sorted(times.values())[1]
+                entries.append(f"    {{{stage}, {n}, {h}, {w}, {c}, {k}, {r}, {s}, {st}, {st}, {pd}, {pd}, {best}}},"
+                               f"   // {net} {sname}: {name(best)} {times[best]:.1f} us, next {runner:.1f} us")
+        del x, wt, z, y, mask, dy, dz, dwt, dx
+        torch.cuda.empty_cache()
+
+    inc = os.path.join(args.out_dir, "cbr_tune_table.inc")
+    with open(inc, "w") as f:
+        f.write("// cbr_tune_table.inc -- per-shape kernel plans measured by the offline tuner\n"
+                "// (conv2d_batchnorm_relu_amd/tune.py).  Each entry: the stage, the layer's shape (N, H, W,\n"
+                "// C, K, R, S, stride_h, stride_w, pad_h, pad_w) and the plan that ran the stage fastest.\n"
+                "// Shapes not listed take the default rule.\n")
+        f.write(f"// command: python -m conv2d_batchnorm_relu_amd.tune {' '.join(argv or sys.argv[1:])}\n")
+        f.write("\n".join(entries) + "\n")
+    md = os.path.join(args.out_dir, "tune_report.md")
+    with open(md, "w") as f:
+        f.write("| net | N | HxW | C->K | RxS/stride | stage | plans (us, median) | chosen | default |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|\n")
+        name = lambda p: lib.cbr_plan_name(p).decode()
+        for net, n, h, w, c, k, r, s, st, pd, sname, times, best, default in report:
+            f.write(f"| {net} | {n} | {h}x{w} | {c}->{k} | {r}x{s}/{st} | {sname} | " +
+                    ", ".join(f"{name(p)} {t:.1f}" for p, t in sorted(times.items(), key=lambda kv: kv[1])) +
+                    f" | {name(best)} | {name(default)} |\n")
+    log(f"wrote {inc} ({len(entries)} entries) and {md}")
+
+
+if __name__ == "__main__":
+    main()

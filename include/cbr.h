@@ -197,6 +197,33 @@ int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
                     uint16_t *y, void *stream);
 
 /*
+ * Kernel plans (tuning interface).  Each convolution stage of a call runs one kernel and
+ * tile shape, its "plan", chosen per shape like the per-shape engine choice of [CBR]
+ * section 7 (empirical search, winner per shape) and [TL]'s autotuned tile
+ * configurations: a compiled-in table of plans measured offline (tune.py), else a
+ * default rule.  Stages: CBR_STAGE_TRAIN_CONV (the conv + statistics of
+ * cbr_forward_train), CBR_STAGE_INFER_CONV (the conv of cbr_forward_infer and of the
+ * conv + bias calls), CBR_STAGE_DGRAD (the data gradient's conv), CBR_STAGE_WGRAD (the
+ * weight gradient).  Plans: 1 persistent 3x3/64-channel conv, 2 first-layer conv,
+ * 3 large-tile 224x256, 4 large-tile 448x128, 5 generic 128x128, 6 generic 128x64,
+ * 7 weight gradient with transposed reads, 8 generic weight gradient.
+ *
+ * cbr_plan_of: the plan the stage will run for this layer shape (> 0), or minus a status.
+ * cbr_plan_eligible: 1 if the plan can run the stage for this shape, 0 if not, or minus
+ *   a status for an invalid shape or stage.
+ * cbr_plan_name: a static name of a plan id.
+ * cbr_set_plan_override: makes the stage run `plan` wherever it is eligible (plan 0
+ *   clears it); process-wide, for the tuner and tests only.  cbr_workspace_bytes follows
+ *   the override, so query it after setting one.  CBR_E_VALUE for a bad stage or plan.
+ */
+enum cbr_stage { CBR_STAGE_TRAIN_CONV = 0, CBR_STAGE_INFER_CONV = 1, CBR_STAGE_DGRAD = 2, CBR_STAGE_WGRAD = 3 };
+
+int cbr_plan_of(const cbr_shape *shape, int stage);
+int cbr_plan_eligible(const cbr_shape *shape, int stage, int plan);
+const char *cbr_plan_name(int plan);
+int cbr_set_plan_override(int stage, int plan);
+
+/*
  * Timed variants for profiling: identical to the calls above, and in addition record
  * caller-created hipEvent_t handles (passed as void*) at the start of the first kernel
  * and the end of the last kernel of each stage (taken from the kernels' own dispatch

@@ -202,3 +202,38 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     assert fn(ctypes.byref(big), *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 5      # CBR_E_WORKSPACE
     assert fn(ctypes.byref(shp(k=12)), *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 3
     assert fn(None, *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 1
+
+
+def test_plan_interface(lib):
+    """Kernel plans: the defaults of the benchmark layers, eligibility, the override and its
+    validation, and the compiled-in table's entries (each eligible for its shape)."""
+    L = cbr._load()
+    L.cbr_plan_name.restype = ctypes.c_char_p
+    name = lambda p: L.cbr_plan_name(p).decode()
+    head = cbr.make_shape(256, 56, 56, 64, 64, 3, 3, 1, 1)
+    stem = cbr.make_shape(64, 224, 224, 3, 64, 7, 7, 2, 3)
+    s4 = cbr.make_shape(256, 14, 14, 256, 256, 3, 3, 1, 1)
+    assert name(L.cbr_plan_of(ctypes.byref(head), 0)) == "persistent_3x3_c64"
+    assert name(L.cbr_plan_of(ctypes.byref(stem), 0)) == "first_layer_c3s2"
+    assert name(L.cbr_plan_of(ctypes.byref(s4), 3)) == "wgrad_transposed_read"
+    assert L.cbr_plan_eligible(ctypes.byref(head), 1, 1) == 0        # no statistics-free persistent form
+    assert L.cbr_plan_eligible(ctypes.byref(head), 0, 7) == 0        # a weight-gradient plan on a conv stage
+    assert L.cbr_plan_of(ctypes.byref(shp(k=12)), 0) == -3
+    assert L.cbr_plan_of(ctypes.byref(head), 9) == -7
+    assert L.cbr_set_plan_override(0, 99) == 7 and L.cbr_set_plan_override(5, 1) == 7
+    try:
+        assert L.cbr_set_plan_override(0, 6) == 0
+        assert name(L.cbr_plan_of(ctypes.byref(head), 0)) == "generic_128x64"
+        small = cbr.cbr_workspace_bytes(stem, cbr.CBR_OP_TRAIN)
+        assert L.cbr_set_plan_override(0, 2) == 0                    # not eligible for s4: ignored there
+        assert name(L.cbr_plan_of(ctypes.byref(s4), 0)) == "large_tile_224x256"
+        assert small > 0
+    finally:
+        L.cbr_set_plan_override(0, 0)
+    assert name(L.cbr_plan_of(ctypes.byref(head), 0)) == "persistent_3x3_c64"
+    table = open(os.path.join(ROOT, "conv2d_batchnorm_relu_amd", "csrc", "cbr_tune_table.inc")).read()
+    for row in re.findall(r"^\s*\{([-\d, ]+)\},", table, flags=re.M):
+        st, n, h, w, c, k, r, s, sh, sw, ph, pw, plan = (int(v) for v in row.split(","))
+        sp = cbr.make_shape(n, h, w, c, k, r, s, sh, ph, stride_w=sw, pad_w=pw)
+        assert L.cbr_plan_eligible(ctypes.byref(sp), st, plan) == 1, row
+        assert L.cbr_plan_of(ctypes.byref(sp), st) == plan, row
