@@ -79,12 +79,13 @@ __global__ __launch_bounds__(NT) void bnbwd_reduce_kernel(const u32x4 *__restric
     }
 }
 
-// dbeta = s1, dgamma = s2 (fp64 over the partial rows, fixed order); coefficients of
-// the apply step: coef[0] = gamma*invstd, coef[1] = dbeta/M, coef[2] = dgamma/M.
-// Block b owns channels 4b..4b+3.
+// dbeta = s1, dgamma = s2 (fp64 over the partial rows, fixed order); the coefficient
+// table of bnbwd_dz8, [5][K]: mean, invstd, ca = gamma*invstd, cb = dbeta/M,
+// cg = dgamma/M.  Block b owns channels 4b..4b+3.
 template <int NTB>
 __global__ __launch_bounds__(NTB) void bnbwd_finalize_kernel(const float *__restrict__ rows, int R, int K, double M,
                                                             const float *__restrict__ gamma,
+                                                            const float *__restrict__ mean,
                                                             const float *__restrict__ invstd,
                                                             float *__restrict__ coef, float *__restrict__ dgamma,
                                                             float *__restrict__ dbeta)
@@ -99,9 +100,11 @@ __global__ __launch_bounds__(NTB) void bnbwd_finalize_kernel(const float *__rest
         const double s2 = e == 0 ? s[4] : e == 1 ? s[5] : e == 2 ? s[6] : s[7];
         dbeta[k] = (float)s1;
         dgamma[k] = (float)s2;
-        coef[k] = gamma[k] * invstd[k];
-        coef[K + k] = (float)(s1 / M);
-        coef[2 * K + k] = (float)(s2 / M);
+        coef[k] = mean[k];
+        coef[K + k] = invstd[k];
+        coef[2 * K + k] = gamma[k] * invstd[k];
+        coef[3 * K + k] = (float)(s1 / M);
+        coef[4 * K + k] = (float)(s2 / M);
     }
 }
 
@@ -111,23 +114,12 @@ template <bool FIXEDK>
 __global__ __launch_bounds__(NT) void bnbwd_apply_kernel(const u32x4 *__restrict__ dy,
                                                          const uint8_t *__restrict__ mask,
                                                          const u32x4 *__restrict__ z,
-                                                         const float *__restrict__ mean,
-                                                         const float *__restrict__ invstd,
                                                          const float *__restrict__ coef, int K,
                                                          u32x4 *__restrict__ dz, int chunks, int cpr)
 {
     const int base = blockIdx.x * NT * APPLY_UNROLL + threadIdx.x;
     float mu[8], is[8], ca[8], cb[8], cg[8];
-    auto load_coef = [&](int k0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            mu[e] = mean[k0 + e];
-            is[e] = invstd[k0 + e];
-            ca[e] = coef[k0 + e];
-            cb[e] = coef[K + k0 + e];
-            cg[e] = coef[2 * K + k0 + e];
-        }
-    };
+    auto load_coef = [&](int k0) { bnbwd_coef8(coef, K, k0, mu, is, ca, cb, cg); };
     if constexpr (FIXEDK) load_coef((threadIdx.x % cpr) * 8);
     u32x4 zv[APPLY_UNROLL], dv[APPLY_UNROLL];
     uint32_t mk[APPLY_UNROLL];
@@ -144,19 +136,7 @@ __global__ __launch_bounds__(NT) void bnbwd_apply_kernel(const u32x4 *__restrict
         const int c = base + u * NT;
         if (c >= chunks) break;
         if constexpr (!FIXEDK) load_coef((c % cpr) * 8);
-        uint32_t o[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int e0 = 2 * h, e1 = 2 * h + 1;
-            const float g0 = ((mk[u] >> e0) & 1u) ? bf16_lo(dv[u][h]) : 0.f;
-            const float g1 = ((mk[u] >> e1) & 1u) ? bf16_hi(dv[u][h]) : 0.f;
-            const float x0 = (bf16_lo(zv[u][h]) - mu[e0]) * is[e0];
-            const float x1 = (bf16_hi(zv[u][h]) - mu[e1]) * is[e1];
-            const float d0 = ca[e0] * (g0 - cb[e0] - x0 * cg[e0]);
-            const float d1 = ca[e1] * (g1 - cb[e1] - x1 * cg[e1]);
-            o[h] = pack_bf16x2(d0, d1);
-        }
-        dz[c] = u32x4{o[0], o[1], o[2], o[3]};
+        dz[c] = bnbwd_dz8(dv[u], zv[u], mk[u], mu, is, ca, cb, cg);
     }
 }
 
@@ -183,20 +163,20 @@ hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *
                           (const u32x4 *)z, saved_mean, saved_invstd, (int)M, K, rows, part);
     if (e != hipSuccess) return e;
     if (Bn <= COLSUM_SMALL_R)
-        e = launch(bnbwd_finalize_kernel<COLSUM_NT_SMALL>, dim3(K / 4), dim3(COLSUM_NT_SMALL), 0, st, nullptr, nullptr,
-                   (const float *)part, Bn, K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
+        e = launch(bnbwd_finalize_kernel<COLSUM_NT_SMALL>, dim3(K / 4), dim3(COLSUM_NT_SMALL), 0, st, nullptr, dz ? nullptr : e1,
+                   (const float *)part, Bn, K, (double)M, gamma, saved_mean, saved_invstd, coef, dgamma, dbeta);
     else
-        e = launch(bnbwd_finalize_kernel<COLSUM_NT_LARGE>, dim3(K / 4), dim3(COLSUM_NT_LARGE), 0, st, nullptr, nullptr,
-                   (const float *)part, Bn, K, (double)M, gamma, saved_invstd, coef, dgamma, dbeta);
-    if (e != hipSuccess) return e;
+        e = launch(bnbwd_finalize_kernel<COLSUM_NT_LARGE>, dim3(K / 4), dim3(COLSUM_NT_LARGE), 0, st, nullptr, dz ? nullptr : e1,
+                   (const float *)part, Bn, K, (double)M, gamma, saved_mean, saved_invstd, coef, dgamma, dbeta);
+    if (e != hipSuccess || !dz) return e;
     const int chunks = (int)(M * K / 8);
     const int cpr = K / 8;
     const int blocks = (chunks + NT * APPLY_UNROLL - 1) / (NT * APPLY_UNROLL);
     if (NT % cpr == 0)
         return launch(bnbwd_apply_kernel<true>, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const u32x4 *)dy, mask,
-                      (const u32x4 *)z, saved_mean, saved_invstd, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
+                      (const u32x4 *)z, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
     return launch(bnbwd_apply_kernel<false>, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const u32x4 *)dy, mask,
-                  (const u32x4 *)z, saved_mean, saved_invstd, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
+                  (const u32x4 *)z, (const float *)coef, K, (u32x4 *)dz, chunks, cpr);
 }
 
 }  // namespace cbr

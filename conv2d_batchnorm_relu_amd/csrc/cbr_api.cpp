@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/cbr.h"
 #include "cbr_launch.h"
@@ -85,18 +86,79 @@ InferLayout infer_layout(const ConvGeom &g)
     return L;
 }
 
+// Bytes of the weight gradient's split partials for plan wplan (0 when it takes one split).
+size_t wgrad_part_bytes(const ConvGeom &g, int wplan)
+{
+    const WgradPlan wp = wgrad_plan(g, wplan);
+    return wp.splits > 1 ? sizeof(float) * (size_t)wp.splits * g.K * g.Kg : 0;
+}
+
+// wplan: the weight-gradient stage's plan; the partials also cover the generic weight
+// gradient when the backward's schedule may form dz inside the gradients (which always
+// runs the generic kernel, whose split count can be larger).
 BwdLayout bwd_layout(const ConvGeom &g, int wplan)
 {
     BwdLayout L;
-    const WgradPlan wp = wgrad_plan(g, wplan);
+    size_t part_bytes = wgrad_part_bytes(g, wplan);
+    if (resolve_plan(g, STAGE_BWD) == PLAN_BWD_FUSED) part_bytes = std::max(part_bytes, wgrad_part_bytes(g, PLAN_WG_GEN));
     size_t o = 0;
     L.dz = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.M * g.K);
     L.part = o; o = align_up(o + sizeof(float) * 2 * g.K * (size_t)bnbwd_blocks(g.M, g.K));
-    L.coef = o; o = align_up(o + sizeof(float) * 3 * g.K);
-    L.wpart = o; o = align_up(o + (wp.splits > 1 ? sizeof(float) * (size_t)wp.splits * g.K * g.Kg : 0));
+    L.coef = o; o = align_up(o + sizeof(float) * 5 * g.K);
+    L.wpart = o; o = align_up(o + part_bytes);
     L.wflip = o; o = align_up(o + sizeof(uint16_t) * (size_t)g.K * g.Kg);
     L.total = o;
     return L;
+}
+
+// A second stream per device for the weight gradient, which runs beside the data
+// gradient (the CBR page runs WGrad on a stream of its own, section 5.2), with the two
+// events that fork it from and join it back to the caller's stream.  Created on first
+// use with the device current and kept for the life of the process; default priority.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;   // held from each event record to the wait that consumes it
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;
+
+SideStream *side_stream()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream &ss = g_side[dev];
+    if (!ss.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+            if (a) hipEventDestroy(a);
+            hipStreamDestroy(st);
+            return nullptr;
+        }
+        ss.fork = a;
+        ss.join = b;
+        ss.stream = st;
+    }
+    return &ss;
+}
+
+// Makes `waiter` wait for everything enqueued so far on `source`, through event ev.
+hipError_t stream_after(hipStream_t waiter, hipStream_t source, hipEvent_t ev)
+{
+    hipError_t e = hipEventRecord(ev, source);
+    if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+    return e;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -313,18 +375,58 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
     if (!aligned16(workspace)) return CBR_E_ALIGN;
 
     hipStream_t s = (hipStream_t)stream;
+    const int bplan = resolve_plan(g, STAGE_BWD);
+    if (bplan == PLAN_BWD_FUSED && !dz) {
+        // No dz tensor: the BN backward stops at its coefficients, and both gradients form
+        // dz from dy, z and the mask as they stage their operands (generic kernels; the
+        // data gradient after the weight gradient, as dx may alias x).
+        float *coef = (float *)ws_at(workspace, L.coef);
+        if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
+                               (float *)ws_at(workspace, L.part), coef, dgamma, dbeta, nullptr, s, ev(events, 0),
+                               ev(events, 1)) != hipSuccess)
+            return CBR_E_HIP;
+        if (launch_conv_wgrad_fused(g, dy, z, (const uint8_t *)relu_mask, coef, x, (float *)ws_at(workspace, L.wpart),
+                                    L.wflip - L.wpart, dw, s, ev(events, 2), ev(events, 3)) != hipSuccess)
+            return CBR_E_HIP;
+        if (dx) {
+            uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
+            if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, ev(events, 4), nullptr) != hipSuccess)
+                return CBR_E_HIP;
+            const ConvGeom d = dgrad_geom(g);
+            if (launch_conv_dgrad_fused(d, dy, z, (const uint8_t *)relu_mask, coef, wt, dx, s, nullptr,
+                                        ev(events, 5)) != hipSuccess)
+                return CBR_E_HIP;
+        } else if (events && (hipEventRecord(ev(events, 4), s) != hipSuccess ||
+                              hipEventRecord(ev(events, 5), s) != hipSuccess)) {
+            return CBR_E_HIP;
+        }
+        return CBR_OK;
+    }
     uint16_t *dzp = dz ? dz : (uint16_t *)ws_at(workspace, L.dz);
-    // masked BN backward (CBR page 5.1) -> WGrad -> DGrad (5.2; skipped for the first layer, 5.3).
-    // WGrad is enqueued before DGrad on the same stream, so it has finished reading x
-    // before DGrad may overwrite it when dx aliases x.
+    // The weight gradient runs beside the data gradient on the side stream when the plan
+    // says so and dx does not overlap x (the data gradient would overwrite what the
+    // weight gradient reads, the in-place hazard of the CBR page's section 5.2);
+    // otherwise both run on the caller's stream, weight gradient first.
+    const size_t xbytes = (size_t)g.N * g.H * g.W * g.C * 2;
+    SideStream *ss = nullptr;
+    if (dx && bplan == PLAN_BWD_OVERLAP && !ranges_overlap(dx, xbytes, x, xbytes))
+        ss = side_stream();
+    // masked BN backward (CBR page 5.1) -> WGrad, DGrad (5.2; DGrad skipped for the first
+    // layer, 5.3).
     if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
                            (float *)ws_at(workspace, L.part),
                            (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s, ev(events, 0),
                            ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    if (launch_conv_wgrad(g, wplan, dzp, x, (float *)ws_at(workspace, L.wpart), dw, s, ev(events, 2),
-                          ev(events, 3)) != hipSuccess)
+    std::unique_lock<std::mutex> side_lock;
+    if (ss) {
+        side_lock = std::unique_lock<std::mutex>(ss->mu);
+        if (stream_after(ss->stream, s, ss->fork) != hipSuccess) return CBR_E_HIP;
+    }
+    if (launch_conv_wgrad(g, wplan, dzp, x, (float *)ws_at(workspace, L.wpart), L.wflip - L.wpart, dw,
+                          ss ? ss->stream : s, ev(events, 2), ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
+    if (ss && hipEventRecord(ss->join, ss->stream) != hipSuccess) return CBR_E_HIP;
     if (dx) {
         uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
         if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, ev(events, 4), nullptr) != hipSuccess) return CBR_E_HIP;
@@ -336,6 +438,8 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
                           hipEventRecord(ev(events, 5), s) != hipSuccess)) {
         return CBR_E_HIP;
     }
+    // the caller's stream continues only once the weight gradient has finished
+    if (ss && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return CBR_E_HIP;
     return CBR_OK;
 }
 

@@ -50,7 +50,7 @@ inline hipError_t launch(Kern k, dim3 grid, dim3 block, uint32_t shmem, hipStrea
 // default rule; every path returns a plan that is eligible for the geometry.  The choice
 // is a pure function of (geometry, stage, override), so workspace sizing and launches
 // agree.
-enum Stage { STAGE_TRAIN = 0, STAGE_INFER = 1, STAGE_DGRAD = 2, STAGE_WGRAD = 3, NSTAGES = 4 };
+enum Stage { STAGE_TRAIN = 0, STAGE_INFER = 1, STAGE_DGRAD = 2, STAGE_WGRAD = 3, STAGE_BWD = 4, NSTAGES = 5 };
 enum Plan {
     PLAN_DEFAULT = 0,
     PLAN_PERSIST3X3 = 1,    // persistent 3x3 / 64-channel conv + statistics (training only)
@@ -61,7 +61,10 @@ enum Plan {
     PLAN_GEN_128X64 = 6,    // generic implicit-GEMM conv, 128 x 64 tiles
     PLAN_WG_TR = 7,         // weight gradient with transposed LDS reads (C % 128, K % 256)
     PLAN_WG_GEN = 8,        // generic weight gradient
-    NPLANS = 9
+    PLAN_BWD_SERIAL = 9,    // backward: weight gradient, then data gradient, one stream
+    PLAN_BWD_OVERLAP = 10,  // backward: weight gradient on a second stream beside the data gradient
+    PLAN_BWD_FUSED = 11,    // backward: no dz tensor; both gradients form dz while staging (K <= 256, C % 8 == 0)
+    NPLANS = 12
 };
 // g is always the layer's geometry (cbr_shape); for STAGE_DGRAD the plan runs, and is
 // checked on, the data gradient's convolution dgrad_geom(g).
@@ -145,17 +148,31 @@ hipError_t launch_bn_fold(int K, int Kg, const uint16_t *w, const float *bias, c
                           uint16_t *w_fold, float *b_fold, hipStream_t st,
                           hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// The masked BN backward: reduce, finalize (dgamma, dbeta and the [5][K] coefficient
+// table of bnbwd_dz8 in coef), then dz unless dz is NULL (the fused gradients form it).
 hipError_t launch_bn_backward(long M, int K, const uint16_t *dy, const uint8_t *mask,
                               const uint16_t *z, const float *gamma, const float *saved_mean,
                               const float *saved_invstd, float *part, float *coef,
                               float *dgamma, float *dbeta, uint16_t *dz, hipStream_t st,
                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// The fused gradients (PLAN_BWD_FUSED): the generic weight-gradient kernel and the
+// generic conv of the data gradient with dz formed on load from dy, z, mask and the
+// [5][K] coefficient table of bnbwd_dz8 (the data gradient's table needs K <= 256).
+hipError_t launch_conv_wgrad_fused(const ConvGeom &g, const uint16_t *dy, const uint16_t *z, const uint8_t *mask,
+                                   const float *bnc, const uint16_t *x, float *part, size_t part_bytes, float *dw,
+                                   hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_conv_dgrad_fused(const ConvGeom &d, const uint16_t *dy, const uint16_t *z, const uint8_t *mask,
+                                   const float *bnc, const uint16_t *wt, uint16_t *dx, hipStream_t st, hipEvent_t e0,
+                                   hipEvent_t e1);
+
 hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt,
                                hipStream_t st, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
+// part: the split partials, part_bytes long; a plan whose splits need more is refused
+// (hipErrorInvalidValue) before any launch.
 hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, const uint16_t *x,
-                             float *part, float *dw, hipStream_t st,
+                             float *part, size_t part_bytes, float *dw, hipStream_t st,
                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 }  // namespace cbr

@@ -42,6 +42,9 @@ bool plan_eligible(const ConvGeom &layer, int stage, int plan)
     case PLAN_GEN_128X64: return is_conv_stage(stage);
     case PLAN_WG_TR: return stage == STAGE_WGRAD && wgrad_tr_eligible(g);
     case PLAN_WG_GEN: return stage == STAGE_WGRAD;
+    case PLAN_BWD_SERIAL: return stage == STAGE_BWD;
+    case PLAN_BWD_OVERLAP: return stage == STAGE_BWD && layer.sh == 1 && layer.sw == 1;
+    case PLAN_BWD_FUSED: return stage == STAGE_BWD && layer.K <= 256 && layer.C % 8 == 0;
     default: return false;
     }
 }
@@ -56,6 +59,7 @@ bool plan_eligible(const ConvGeom &layer, int stage, int plan)
 int default_plan(const ConvGeom &layer, int stage)
 {
     if (stage == STAGE_WGRAD) return wgrad_tr_eligible(layer) ? PLAN_WG_TR : PLAN_WG_GEN;
+    if (stage == STAGE_BWD) return PLAN_BWD_SERIAL;
     if (stage == STAGE_TRAIN && halo_eligible(layer)) return PLAN_PERSIST3X3;
     if (stage == STAGE_TRAIN && c3s2_eligible(layer)) return PLAN_FIRST_LAYER;
     const ConvGeom g = stage == STAGE_DGRAD ? dgrad_geom(layer) : layer;
@@ -92,6 +96,9 @@ const char *plan_name(int plan)
     case PLAN_GEN_128X64: return "generic_128x64";
     case PLAN_WG_TR: return "wgrad_transposed_read";
     case PLAN_WG_GEN: return "wgrad_generic";
+    case PLAN_BWD_SERIAL: return "backward_serial";
+    case PLAN_BWD_OVERLAP: return "backward_wgrad_beside_dgrad";
+    case PLAN_BWD_FUSED: return "backward_dz_formed_in_gradients";
     default: return "unknown";
     }
 }

@@ -38,7 +38,15 @@ struct ConvParams {
     const float *bias;
     uint16_t *out;
     float *partials;
+    // FUSE: the input is dz, formed on load from the backward's dy, z, mask and its
+    // [5][C] coefficient table (x unused)
+    const uint16_t *dy, *z;
+    const uint8_t *mask;
+    const float *bnc;
 };
+
+// Channels of dz the fused form's coefficient table holds in LDS.
+constexpr int FUSE_MAXC = 256;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -57,7 +65,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-template <int BM, int BN, int MODE, int EPI>
+// FUSE (the data gradient of a backward that keeps no dz tensor): the A operand is dz,
+// formed while staging from dy, the stored z and the ReLU mask (bnbwd_dz8, the same
+// arithmetic as the BN-backward apply), zero at padding positions.
+template <int BM, int BN, int MODE, int EPI, bool FUSE = false>
 __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
 {
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -70,6 +81,8 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
     static_assert(BM * LDO <= 2 * STAGE, "epilogue tile must fit the staging buffers");
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
     __shared__ float sstat[2][2][BN];
+    __shared__ __attribute__((aligned(16))) float sbn[FUSE ? 5 * FUSE_MAXC : 4];
+    static_assert(!FUSE || MODE != GATHER_SCALAR, "the fused form gathers 16-byte channel chunks");
 
     const ConvGeom &g = prm.g;
     const uint16_t *__restrict__ x = prm.x;
@@ -98,7 +111,14 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
             a_hb[j] = -0x40000000; a_wb[j] = 0; a_nb[j] = -1;   // never inside the image
         }
     }
-    const __amdgpu_buffer_rsrc_t xr = rsrc_of(x, (uint32_t)((size_t)g.N * g.H * g.W * g.C * 2));
+    const uint32_t xbytes = (uint32_t)((size_t)g.N * g.H * g.W * g.C * 2);
+    const __amdgpu_buffer_rsrc_t xr = rsrc_of(FUSE ? prm.dy : x, xbytes);
+    const __amdgpu_buffer_rsrc_t zr = rsrc_of(prm.z, FUSE ? xbytes : 0u);
+    const __amdgpu_buffer_rsrc_t mr = rsrc_of(prm.mask, FUSE ? xbytes / 16 : 0u);
+    if constexpr (FUSE) {
+        for (int i = tid; i < 5 * g.C; i += NT) sbn[i] = prm.bnc[i];
+        __syncthreads();
+    }
     const __amdgpu_buffer_rsrc_t wr = rsrc_of(wt, (uint32_t)((size_t)g.K * g.Kg * 2));
     // Byte offset of each A row's pixel (tap 0, channel grp*8) and each B row's start.
     int a_off[AI], b_off[AI > BI ? AI : BI];
@@ -111,7 +131,20 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
     }
 
     u32x4 ra2[2][AI], rb2[2][BI];
+    // FUSE: the z chunks and mask bytes beside the dy chunks in ra2, and which rows are
+    // inside the image (bit j)
+    u32x4 rz2[2][FUSE ? AI : 1];
+    uint32_t rm2[2][FUSE ? AI : 1], okm2[2] = {0u, 0u};
+    auto load_a = [&](int set, int j, bool ok, int off, u32x4 (&ra)[AI]) {
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? off : (int)OOB, 0, 0);
+        if constexpr (FUSE) {
+            rz2[set][j] = __builtin_amdgcn_raw_buffer_load_b128(zr, ok ? off : (int)OOB, 0, 0);
+            rm2[set][j] = __builtin_amdgcn_raw_buffer_load_b8(mr, ok ? off >> 4 : (int)OOB, 0, 0);
+            okm2[set] = ok ? okm2[set] | (1u << j) : okm2[set] & ~(1u << j);
+        }
+    };
     auto load = [&](int ks, u32x4 (&ra)[AI], u32x4 (&rb)[BI]) {
+        const int set = &ra == &ra2[0] ? 0 : 1;
         const int kk0 = ks * BK + grp * 8;
         if constexpr (MODE == GATHER_TAP) {
             // Uniform tap (r, s) and channel base of this K-step.
@@ -123,7 +156,7 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
             for (int j = 0; j < AI; ++j) {
                 const int h = a_hb[j] + r, w = a_wb[j] + s;
                 const bool ok = (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-                ra[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? a_off[j] + toff : (int)OOB, 0, 0);
+                load_a(set, j, ok, a_off[j] + toff, ra);
             }
 #pragma unroll
             for (int j = 0; j < BI; ++j)
@@ -142,7 +175,7 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
             for (int j = 0; j < AI; ++j) {
                 const int h = a_hb[j] + r, w = a_wb[j] + s;
                 const bool ok = kok && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-                ra[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? a_off[j] + toff : (int)OOB, 0, 0);
+                load_a(set, j, ok, a_off[j] + toff, ra);
             }
 #pragma unroll
             for (int j = 0; j < BI; ++j)
@@ -183,11 +216,26 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
             }
         }
     };
-    auto store = [&](int buf, const u32x4 (&ra)[AI], const u32x4 (&rb)[BI]) {
+    // ks: the k-step whose data the register set holds (FUSE: picks the dz channels)
+    auto store = [&](int buf, const u32x4 (&ra)[AI], const u32x4 (&rb)[BI], int ks) {
         uint16_t *sa = smem + buf * STAGE;
         uint16_t *sb = sa + BM * LDK;
+        if constexpr (FUSE) {
+            const int set = &ra == &ra2[0] ? 0 : 1;
+            const int kk0 = ks * BK + grp * 8;
+            const int ch = kk0 < g.Kg ? kk0 - (kk0 / g.C) * g.C : 0;
+            float mu[8], is[8], ca[8], cb[8], cg[8];
+            bnbwd_coef8(sbn, g.C, ch, mu, is, ca, cb, cg);
 #pragma unroll
-        for (int j = 0; j < AI; ++j) *(u32x4 *)(sa + (rbase + RPP * j) * LDK + grp * 8) = ra[j];
+            for (int j = 0; j < AI; ++j) {
+                const u32x4 d = bnbwd_dz8(ra[j], rz2[set][j], rm2[set][j], mu, is, ca, cb, cg);
+                *(u32x4 *)(sa + (rbase + RPP * j) * LDK + grp * 8) =
+                    ((okm2[set] >> j) & 1u) ? d : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < AI; ++j) *(u32x4 *)(sa + (rbase + RPP * j) * LDK + grp * 8) = ra[j];
+        }
 #pragma unroll
         for (int j = 0; j < BI; ++j) *(u32x4 *)(sb + (rbase + RPP * j) * LDK + grp * 8) = rb[j];
     };
@@ -235,17 +283,17 @@ __global__ __launch_bounds__(NT, 2) void conv_fprop_kernel(ConvParams prm)
     const int ksteps = (g.Kg + BK - 1) / BK;
     load(0, ra2[0], rb2[0]);
     if (ksteps > 1) load(1, ra2[1], rb2[1]);
-    store(0, ra2[0], rb2[0]);
+    store(0, ra2[0], rb2[0], 0);
     __syncthreads();
     for (int ks = 0; ks < ksteps; ks += 2) {
         if (ks + 2 < ksteps) load(ks + 2, ra2[0], rb2[0]);
         compute(0);
-        if (ks + 1 < ksteps) store(1, ra2[1], rb2[1]);
+        if (ks + 1 < ksteps) store(1, ra2[1], rb2[1], ks + 1);
         __syncthreads();
         if (ks + 1 >= ksteps) break;
         if (ks + 3 < ksteps) load(ks + 3, ra2[1], rb2[1]);
         compute(1);
-        if (ks + 2 < ksteps) store(0, ra2[0], rb2[0]);
+        if (ks + 2 < ksteps) store(0, ra2[0], rb2[0], ks + 2);
         __syncthreads();
     }
 
@@ -351,6 +399,19 @@ hipError_t launch_mode(const ConvGeom &g, int epi, const ConvParams &prm, dim3 g
 
 }  // namespace
 
+hipError_t launch_conv_dgrad_fused(const ConvGeom &d, const uint16_t *dy, const uint16_t *z, const uint8_t *mask,
+                                   const float *bnc, const uint16_t *wt, uint16_t *dx, hipStream_t st, hipEvent_t e0,
+                                   hipEvent_t e1)
+{
+    // 128 x 64 tiles: the 128 x 128 form holds too many registers with the dz staging
+    const ConvPlan p = conv_plan(d, PLAN_GEN_128X64);
+    ConvParams prm{d, nullptr, wt, nullptr, dx, nullptr, dy, z, mask, bnc};
+    dim3 grid(p.tiles_m, p.tiles_n);
+    return d.C % 64 == 0
+               ? launch(conv_fprop_kernel<128, 64, GATHER_TAP, EPI_PLAIN, true>, grid, dim3(NT), 0, st, e0, e1, prm)
+               : launch(conv_fprop_kernel<128, 64, GATHER_VEC, EPI_PLAIN, true>, grid, dim3(NT), 0, st, e0, e1, prm);
+}
+
 ConvPlan conv_plan(const ConvGeom &g, int plan)
 {
     ConvPlan p;
@@ -369,7 +430,7 @@ hipError_t launch_conv_fprop(const ConvGeom &g, int epi, int plan, const uint16_
     if (plan == PLAN_IG_224X256 || plan == PLAN_IG_448X128)
         return launch_conv_igemm(g, epi, plan, x, w, bias, out, partials, st, e0, e1);
     const ConvPlan p = conv_plan(g, plan);
-    ConvParams prm{g, x, w, bias, out, partials};
+    ConvParams prm{g, x, w, bias, out, partials, nullptr, nullptr, nullptr, nullptr};
     dim3 grid(p.tiles_m, p.tiles_n);
     if (p.bn == 128) return launch_mode<128, 128>(g, epi, prm, grid, st, e0, e1);
     return launch_mode<128, 64>(g, epi, prm, grid, st, e0, e1);

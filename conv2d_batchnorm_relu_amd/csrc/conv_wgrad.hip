@@ -47,6 +47,11 @@ struct WgradParams {
     float *out;            // [splits][K][Kg] (or dw itself when splits == 1)
     int rows_per_split;
     FastDiv dpq, dq;       // division by P*Q and by Q
+    // FUSE: dz formed on load from the backward's dy, z, mask and its [5][K] coefficient
+    // table (dz unused)
+    const uint16_t *dy, *z;
+    const uint8_t *mask;
+    const float *bnc;
 };
 
 __device__ __forceinline__ int swz(int row, int m)   // element offset of (row, m) in a tile row
@@ -63,7 +68,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BMK, int BNC, bool VEC, int STAGES>
+// FUSE (the weight gradient of a backward that keeps no dz tensor): the dz operand is
+// formed while staging from dy, the stored z and the ReLU mask (bnbwd_dz8, the same
+// arithmetic as the BN-backward apply).
+template <int BMK, int BNC, bool VEC, int STAGES, bool FUSE = false>
 __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
 {
     constexpr int WM = BMK / 2, WN = BNC / 2;
@@ -81,7 +89,23 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
     const int k0 = blockIdx.y * BMK, n0 = blockIdx.x * BNC;
     const int mbeg = blockIdx.z * prm.rows_per_split;
     const int mend = min(g.M, mbeg + prm.rows_per_split);
-    const __amdgpu_buffer_rsrc_t dzr = rsrc_of(prm.dz, (uint32_t)((size_t)g.M * g.K * 2));
+    const uint32_t zbytes = (uint32_t)((size_t)g.M * g.K * 2);
+    const __amdgpu_buffer_rsrc_t dzr = rsrc_of(FUSE ? prm.dy : prm.dz, zbytes);
+    const __amdgpu_buffer_rsrc_t zr = rsrc_of(prm.z, FUSE ? zbytes : 0u);
+    const __amdgpu_buffer_rsrc_t mr = rsrc_of(prm.mask, FUSE ? zbytes / 16 : 0u);
+    // FUSE: the coefficient table of this workgroup's BMK channels, [5][BMK]
+    __shared__ __attribute__((aligned(16))) float sbn[FUSE ? 5 * BMK : 4];
+    if constexpr (FUSE) {
+        for (int i = tid; i < 5 * BMK; i += NT) {
+            const int t = i / BMK, k = k0 + i - t * BMK;
+            sbn[i] = k < g.K ? prm.bnc[t * g.K + k] : 0.f;
+        }
+        __syncthreads();
+    }
+    // FUSE: z chunks and mask bytes beside the dy chunks, and which (item, pixel) are in
+    // range (bit 2j + h), per register set
+    u32x4 rz2[2][FUSE ? AI : 1][2];
+    uint32_t rm2[2][FUSE ? AI : 1][2], okm2[2] = {0u, 0u};
     const __amdgpu_buffer_rsrc_t xr = rsrc_of(x, (uint32_t)((size_t)g.N * g.H * g.W * g.C * 2));
 
     // item i -> (pixel pair p, chunk cc): within a wave, 8 pairs x 8 chunks.
@@ -101,7 +125,7 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
         b_s[j] = tap - b_r[j] * g.S;
     }
 
-    auto load = [&](int mstep, u32x4 (&ra)[AI][2], u32x4 (&rb)[BI][2]) {
+    auto load = [&](int mstep, int set, u32x4 (&ra)[AI][2], u32x4 (&rb)[BI][2]) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int it = tid + NT * j;
@@ -110,7 +134,14 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
             for (int h = 0; h < 2; ++h) {
                 const int m = mstep + 2 * item_p(it) + h;
                 const bool ok = m < mend && k < g.K;
-                ra[j][h] = __builtin_amdgcn_raw_buffer_load_b128(dzr, ok ? 2 * (m * g.K + k) : (int)OOB, 0, 0);
+                const int off = ok ? 2 * (m * g.K + k) : (int)OOB;
+                ra[j][h] = __builtin_amdgcn_raw_buffer_load_b128(dzr, off, 0, 0);
+                if constexpr (FUSE) {
+                    rz2[set][j][h] = __builtin_amdgcn_raw_buffer_load_b128(zr, off, 0, 0);
+                    rm2[set][j][h] = __builtin_amdgcn_raw_buffer_load_b8(mr, ok ? off >> 4 : (int)OOB, 0, 0);
+                    const uint32_t bit = 1u << (2 * j + h);
+                    okm2[set] = ok ? okm2[set] | bit : okm2[set] & ~bit;
+                }
             }
         }
 #pragma unroll
@@ -151,16 +182,26 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
     };
     // Transposed store: channel-chunk element e of pixels (2p, 2p+1) -> row 8*cc + e,
     // columns 2p and 2p+1 (one 32-bit LDS write).
-    auto store = [&](int buf, const u32x4 (&ra)[AI][2], const u32x4 (&rb)[BI][2]) {
+    auto store = [&](int buf, int set, const u32x4 (&ra)[AI][2], const u32x4 (&rb)[BI][2]) {
         uint16_t *sa = smem + buf * STAGE;
         uint16_t *sb = sa + BMK * LDK;
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int it = tid + NT * j, p = item_p(it), cc = item_c(it);
+            u32x4 d[2] = {ra[j][0], ra[j][1]};
+            if constexpr (FUSE) {
+                float mu[8], is[8], ca[8], cb[8], cg[8];
+                bnbwd_coef8(sbn, BMK, 8 * cc, mu, is, ca, cb, cg);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 v = bnbwd_dz8(ra[j][h], rz2[set][j][h], rm2[set][j][h], mu, is, ca, cb, cg);
+                    d[h] = ((okm2[set] >> (2 * j + h)) & 1u) ? v : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (ra[j][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t hi = (ra[j][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t lo = (d[0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t hi = (d[1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
                 *(uint32_t *)(sa + swz(8 * cc + e, 2 * p)) = lo | (hi << 16);
             }
         }
@@ -216,35 +257,35 @@ __global__ __launch_bounds__(NT, 2) void conv_wgrad_kernel(WgradParams prm)
         // Two register stages: the loads of a K-step are issued two K-steps ahead.
         u32x4 ra2[2][AI][2], rb2[2][BI][2];
         if (nsteps > 0) {
-            load(mbeg, ra2[0], rb2[0]);
-            if (nsteps > 1) load(mbeg + BKM, ra2[1], rb2[1]);
-            store(0, ra2[0], rb2[0]);
+            load(mbeg, 0, ra2[0], rb2[0]);
+            if (nsteps > 1) load(mbeg + BKM, 1, ra2[1], rb2[1]);
+            store(0, 0, ra2[0], rb2[0]);
         }
         __syncthreads();
         for (int st = 0; st < nsteps; st += 2) {
-            if (st + 2 < nsteps) load(mbeg + (st + 2) * BKM, ra2[0], rb2[0]);
+            if (st + 2 < nsteps) load(mbeg + (st + 2) * BKM, 0, ra2[0], rb2[0]);
             compute(0);
-            if (st + 1 < nsteps) store(1, ra2[1], rb2[1]);
+            if (st + 1 < nsteps) store(1, 1, ra2[1], rb2[1]);
             __syncthreads();
             if (st + 1 >= nsteps) break;
-            if (st + 3 < nsteps) load(mbeg + (st + 3) * BKM, ra2[1], rb2[1]);
+            if (st + 3 < nsteps) load(mbeg + (st + 3) * BKM, 1, ra2[1], rb2[1]);
             compute(1);
-            if (st + 2 < nsteps) store(0, ra2[0], rb2[0]);
+            if (st + 2 < nsteps) store(0, 0, ra2[0], rb2[0]);
             __syncthreads();
         }
     } else {
         // One register stage: the loads of a K-step are issued one K-step ahead.
         u32x4 ra[AI][2], rb[BI][2];
         if (nsteps > 0) {
-            load(mbeg, ra, rb);
-            store(0, ra, rb);
+            load(mbeg, 0, ra, rb);
+            store(0, 0, ra, rb);
         }
         __syncthreads();
         for (int st = 0; st < nsteps; ++st) {
             const int cur = st & 1;
-            if (st + 1 < nsteps) load(mbeg + (st + 1) * BKM, ra, rb);
+            if (st + 1 < nsteps) load(mbeg + (st + 1) * BKM, 0, ra, rb);
             compute(cur);
-            if (st + 1 < nsteps) store(cur ^ 1, ra, rb);
+            if (st + 1 < nsteps) store(cur ^ 1, 0, ra, rb);
             __syncthreads();
         }
     }
@@ -603,10 +644,43 @@ WgradPlan wgrad_plan(const ConvGeom &g, int plan)
     return p;
 }
 
+// The generic weight-gradient kernel for plan p, then the fixed-order split sum.
+template <bool FUSE>
+hipError_t launch_wgrad_generic(const ConvGeom &g, const WgradPlan &p, const WgradParams &prm, float *part, float *dw,
+                                hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+{
+    dim3 grid(p.tiles_n, p.tiles_m, p.splits);
+    const bool vec = (g.C % 8) == 0;
+    const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;   // end event on the last kernel of the stage
+    hipError_t e;
+    if constexpr (FUSE) {   // C % 8 == 0 (the fused plan's condition): 16-byte gathers of x
+        e = p.bm == 128 ? launch(conv_wgrad_kernel<128, 128, true, WGRAD_STAGES_128, true>, grid, dim3(NT), 0, st, e0,
+                                 ek, prm)
+                        : launch(conv_wgrad_kernel<64, 128, true, 2, true>, grid, dim3(NT), 0, st, e0, ek, prm);
+    } else if (p.bm == 128) {
+        e = vec ? launch(conv_wgrad_kernel<128, 128, true, WGRAD_STAGES_128>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<128, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
+    } else {
+        e = vec ? launch(conv_wgrad_kernel<64, 128, true, 2>, grid, dim3(NT), 0, st, e0, ek, prm)
+                : launch(conv_wgrad_kernel<64, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
+    }
+    if (e != hipSuccess || p.splits == 1) return e;
+    const long n = (long)g.K * g.Kg;
+    const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);
+    return launch(split_sum_kernel, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const float *)part, p.splits, n, dw);
+}
+
+// Whether the split partials of plan p fit a buffer of part_bytes.
+bool parts_fit(const ConvGeom &g, const WgradPlan &p, size_t part_bytes)
+{
+    return p.splits <= 1 || sizeof(float) * (size_t)p.splits * g.K * g.Kg <= part_bytes;
+}
+
 hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, const uint16_t *x, float *part,
-                             float *dw, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+                             size_t part_bytes, float *dw, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
     const WgradPlan p = wgrad_plan(g, plan);
+    if (!parts_fit(g, p, part_bytes)) return hipErrorInvalidValue;
     if (p.tr) {
         WgradTrParams tp;
         tp.dz = dz;
@@ -629,22 +703,20 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, co
         return launch(split_sum_kernel, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const float *)part, p.splits, n,
                       dw);
     }
-    WgradParams prm{g, dz, x, p.splits == 1 ? dw : part, p.rows_per_split, fast_div((uint32_t)(g.P * g.Q)),
-                    fast_div((uint32_t)g.Q)};
-    dim3 grid(p.tiles_n, p.tiles_m, p.splits);
-    const bool vec = (g.C % 8) == 0;
-    const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;   // end event on the last kernel of the stage
-    hipError_t e;
-    if (p.bm == 128)
-        e = vec ? launch(conv_wgrad_kernel<128, 128, true, WGRAD_STAGES_128>, grid, dim3(NT), 0, st, e0, ek, prm)
-                : launch(conv_wgrad_kernel<128, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
-    else
-        e = vec ? launch(conv_wgrad_kernel<64, 128, true, 2>, grid, dim3(NT), 0, st, e0, ek, prm)
-                : launch(conv_wgrad_kernel<64, 128, false, 1>, grid, dim3(NT), 0, st, e0, ek, prm);
-    if (e != hipSuccess || p.splits == 1) return e;
-    const long n = (long)g.K * g.Kg;
-    const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);
-    return launch(split_sum_kernel, dim3(blocks), dim3(NT), 0, st, nullptr, e1, (const float *)part, p.splits, n, dw);
+    WgradParams prm{g,       dz,      x,       p.splits == 1 ? dw : part, p.rows_per_split, fast_div((uint32_t)(g.P * g.Q)),
+                    fast_div((uint32_t)g.Q), nullptr, nullptr, nullptr, nullptr};
+    return launch_wgrad_generic<false>(g, p, prm, part, dw, st, e0, e1);
+}
+
+hipError_t launch_conv_wgrad_fused(const ConvGeom &g, const uint16_t *dy, const uint16_t *z, const uint8_t *mask,
+                                   const float *bnc, const uint16_t *x, float *part, size_t part_bytes, float *dw,
+                                   hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+{
+    const WgradPlan p = wgrad_plan(g, PLAN_WG_GEN);
+    if (!parts_fit(g, p, part_bytes)) return hipErrorInvalidValue;
+    WgradParams prm{g,       nullptr, x,  p.splits == 1 ? dw : part, p.rows_per_split, fast_div((uint32_t)(g.P * g.Q)),
+                    fast_div((uint32_t)g.Q), dy, z,  mask, bnc};
+    return launch_wgrad_generic<true>(g, p, prm, part, dw, st, e0, e1);
 }
 
 hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt, hipStream_t st,

@@ -4,16 +4,18 @@ configurations).
 
 For every layer shape of a list (the conv layers of ResNet-50 and VGG16-BN at the given
 batch sizes) and every stage of a call -- the training forward's conv, the inference
-conv, the data gradient, the weight gradient -- it times each plan the library reports
+conv, the data gradient, the weight gradient, the backward's schedule -- it times each plan the library reports
 eligible (cbr_plan_eligible), forcing it with cbr_set_plan_override, and keeps the
 fastest.  It writes the table that csrc/cbr_plan.cpp compiles in (cbr_tune_table.inc)
 and a markdown summary of every timing.  Rebuild the library after replacing the table.
 
-    python -m conv2d_batchnorm_relu_amd.tune --out-dir gpurun_out/tune [--batch 32 256] [--reps 15]
+    python -m conv2d_batchnorm_relu_amd.tune --out-dir gpurun_out/tune [--batch 32 256] [--reps 10]
 
-Timings are HIP events on the kernels' own dispatch packets (the _ev calls), median of
---reps calls after a warm-up, on synthetic N(0,1) inputs (values do not change the
-kernels' work).
+A stage's plans are compared by the time of the whole call that contains the stage (the
+training forward, the conv + bias + ReLU call, the backward), measured with HIP events
+around --reps back-to-back calls (median of three such runs, after a warm-up), so the
+figure is the GPU's time per call rather than the host's enqueue time.  Inputs are
+synthetic N(0,1) tensors (values do not change the kernels' work).
 """
 from __future__ import annotations
 
@@ -24,8 +26,8 @@ import statistics
 import sys
 import time
 
-STAGES = {0: "train_conv", 1: "infer_conv", 2: "dgrad", 3: "wgrad"}
-PLANS = range(1, 9)
+STAGES = {0: "train_conv", 1: "infer_conv", 2: "dgrad", 3: "wgrad", 4: "backward"}
+PLANS = range(1, 12)
 
 
 def resnet50_layers():
@@ -57,7 +59,7 @@ def main(argv=None):
     ap.add_argument("--out-dir", default="gpurun_out/tune")
     ap.add_argument("--batch", type=int, nargs="+", default=[32, 256])
     ap.add_argument("--vgg-batch", type=int, nargs="+", default=[32])
-    ap.add_argument("--reps", type=int, default=15)
+    ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--max-elems", type=int, default=1 << 29, help="skip layers whose tensors exceed this")
     args = ap.parse_args(argv)
@@ -72,12 +74,6 @@ def main(argv=None):
 
     def log(msg):
         print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
-
-    def events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for e in evs:
-            e.record()
-        return evs
 
     layers = [("resnet50", n, L) for n in args.batch for L in resnet50_layers()]
     layers += [("vgg16bn", n, L) for n in args.vgg_batch for L in vgg16_layers()]
@@ -103,46 +99,54 @@ def main(argv=None):
         dwt = torch.empty(k, r, s, c, device=dev)
         dx = torch.empty_like(x) if st == 1 else None
 
+        ws_t = ws_b = None
+
         def run_train(ev):
-            ws = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_TRAIN)), dtype=torch.uint8, device=dev)
             cbr.cbr_forward_train(sp, x, wt, vk[0], vk[1], vk[2], vk[3], 1e-5, 0.1, z, y, mask, vk[4], vk[5],
-                                  vk[2], vk[3], ws, events=ev)
-            return ws
+                                  vk[2], vk[3], ws_t, events=ev)
 
         def run_infer(ev):
             cbr.cbr_conv2d_bias_relu(sp, x, wt, vk[0], y, events=ev)
 
         def run_bwd(ev):
-            ws = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_BWD)), dtype=torch.uint8, device=dev)
-            cbr.cbr_backward(sp, x, wt, z, mask, dy, vk[0], vk[4], vk[5], dz, vk[1], vk[2], dwt, dx, ws, events=ev)
-            return ws
+            cbr.cbr_backward(sp, x, wt, z, mask, dy, vk[0], vk[4], vk[5], dz, vk[1], vk[2], dwt, dx, ws_b, events=ev)
 
+        def run_bwd_nodz(ev):   # the backward's schedule is compared without a dz output
+            cbr.cbr_backward(sp, x, wt, z, mask, dy, vk[0], vk[4], vk[5], None, vk[1], vk[2], dwt, dx, ws_b, events=ev)
+
+        def workspaces():
+            t = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_TRAIN)), dtype=torch.uint8, device=dev)
+            b = torch.empty(max(256, cbr.cbr_workspace_bytes(sp, cbr.CBR_OP_BWD)), dtype=torch.uint8, device=dev)
+            return t, b
+
+        ws_t, ws_b = workspaces()
         run_train(None)   # a z, mask and saved statistics for the backward
         torch.cuda.synchronize()
         for stage, sname in STAGES.items():
-            if stage == 2 and st != 1:
+            if stage in (2, 4) and st != 1:
                 continue   # the data gradient needs stride 1
             cands = [p for p in PLANS if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
             default = lib.cbr_plan_of(ctypes.byref(sp), stage)
             times = {}
+            # a stage's plan is judged by the whole call that contains it, timed over
+            # back-to-back calls (the GPU's time per call, not the host's enqueue time)
+            fn = run_train if stage == 0 else run_infer if stage == 1 else run_bwd if stage < 4 else run_bwd_nodz
             for plan in cands:
                 lib.cbr_set_plan_override(stage, plan)
-                fn, nev, pair = ((run_train, 6, None) if stage == 0 else (run_infer, 2, (0, 1)) if stage == 1
-                                 else (run_bwd, 6, (4, 5) if stage == 2 else (2, 3)))
                 try:
+                    ws_t, ws_b = workspaces()
                     for _ in range(args.warmup):
                         fn(None)
-                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     ts = []
-                    for _ in range(args.reps):
-                        ev = events(nev)
-                        keep = fn(ev)
+                    for _ in range(3):
                         torch.cuda.synchronize()
-                        if pair is None:
-                            ts.append(ev[0].elapsed_time(ev[5]) * 1000.0)
-                        else:
-                            ts.append(ev[pair[0]].elapsed_time(ev[pair[1]]) * 1000.0)
-                        del keep
+                        e0.record()
+                        for _ in range(args.reps):
+                            fn(None)
+                        e1.record()
+                        torch.cuda.synchronize()
+                        ts.append(e0.elapsed_time(e1) * 1000.0 / args.reps)
                     times[plan] = statistics.median(ts)
                 finally:
                     lib.cbr_set_plan_override(stage, 0)
@@ -158,7 +162,7 @@ def main(argv=None):
                 runner = sorted(times.values())[1]
                 entries.append(f"    {{{stage}, {n}, {h}, {w}, {c}, {k}, {r}, {s}, {st}, {st}, {pd}, {pd}, {best}}},"
                                f"   // {net} {sname}: {name(best)} {times[best]:.1f} us, next {runner:.1f} us")
-        del x, wt, z, y, mask, dy, dz, dwt, dx
+        del x, wt, z, y, mask, dy, dz, dwt, dx, ws_t, ws_b
         torch.cuda.empty_cache()
 
     inc = os.path.join(args.out_dir, "cbr_tune_table.inc")

@@ -144,6 +144,10 @@ int cbr_forward_infer(const cbr_shape *shape,
  * form of [CBR] 5.3, which skips the data gradient.  dx may alias x: the weight
  * gradient finishes reading x before the data gradient writes dx ([CBR] 5.2).
  * A non-NULL dx needs stride 1 in both directions.
+ * When dx does not overlap x the weight gradient may run on a second stream that the
+ * library keeps per device (forked from and joined back to `stream` with events, see
+ * CBR_STAGE_BWD); the call's work is still complete when `stream` reaches its end.
+ * Calls on one device from several host threads serialise their enqueueing around it.
  */
 int cbr_backward(const cbr_shape *shape,
                  const uint16_t *x, const uint16_t *w, const uint16_t *z,
@@ -204,9 +208,16 @@ int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
  * default rule.  Stages: CBR_STAGE_TRAIN_CONV (the conv + statistics of
  * cbr_forward_train), CBR_STAGE_INFER_CONV (the conv of cbr_forward_infer and of the
  * conv + bias calls), CBR_STAGE_DGRAD (the data gradient's conv), CBR_STAGE_WGRAD (the
- * weight gradient).  Plans: 1 persistent 3x3/64-channel conv, 2 first-layer conv,
- * 3 large-tile 224x256, 4 large-tile 448x128, 5 generic 128x128, 6 generic 128x64,
- * 7 weight gradient with transposed reads, 8 generic weight gradient.
+ * weight gradient), CBR_STAGE_BWD (how cbr_backward schedules its gradients).  Plans:
+ * 1 persistent 3x3/64-channel conv, 2 first-layer conv, 3 large-tile 224x256,
+ * 4 large-tile 448x128, 5 generic 128x128, 6 generic 128x64, 7 weight gradient with
+ * transposed reads, 8 generic weight gradient, 9 backward on one stream (weight gradient,
+ * then data gradient), 10 backward with the weight gradient on a second stream beside the
+ * data gradient ([CBR] section 5.2's WGrad stream; used only when dx does not overlap x,
+ * else the call falls back to 9), 11 backward with no dz tensor: both gradients form dz
+ * from dy, z and the mask while staging their operands ([CBR] section 5.1 keeps the
+ * masked gradient on chip; K <= 256 and C % 8 == 0; used only when dz is NULL, else
+ * the call falls back to 9).
  *
  * cbr_plan_of: the plan the stage will run for this layer shape (> 0), or minus a status.
  * cbr_plan_eligible: 1 if the plan can run the stage for this shape, 0 if not, or minus
@@ -216,7 +227,8 @@ int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
  *   clears it); process-wide, for the tuner and tests only.  cbr_workspace_bytes follows
  *   the override, so query it after setting one.  CBR_E_VALUE for a bad stage or plan.
  */
-enum cbr_stage { CBR_STAGE_TRAIN_CONV = 0, CBR_STAGE_INFER_CONV = 1, CBR_STAGE_DGRAD = 2, CBR_STAGE_WGRAD = 3 };
+enum cbr_stage { CBR_STAGE_TRAIN_CONV = 0, CBR_STAGE_INFER_CONV = 1, CBR_STAGE_DGRAD = 2, CBR_STAGE_WGRAD = 3,
+                 CBR_STAGE_BWD = 4 };
 
 int cbr_plan_of(const cbr_shape *shape, int stage);
 int cbr_plan_eligible(const cbr_shape *shape, int stage, int plan);

@@ -39,7 +39,7 @@ def lib():
 
 def eligible(g, stage):
     sp = H.cshape(g)
-    return [p for p in range(1, 9) if lib().cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
+    return [p for p in range(1, 12) if lib().cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
 
 
 class forced:
@@ -89,8 +89,12 @@ def test_infer_conv_plan(g, plan):
     H.assert_close(y, H.oracle.conv2d_bias_act(H.oshape(g), d["x"], d["w"], d["bias"], True), "conv+bias+relu")
 
 
-@pytest.mark.parametrize("stage", [2, 3], ids=["dgrad", "wgrad"])
-@pytest.mark.parametrize("g", PLAN_GEOMS[:4], ids=str)
+@pytest.mark.parametrize("stage", [2, 3, 4], ids=["dgrad", "wgrad", "schedule"])
+# + a stride-2 layer (no data gradient) and a layer whose generic weight gradient splits
+# the pixels more finely (15 splits) than the transposed-read one (12): the fused schedule
+# runs the generic kernel, so the workspace must hold its partials.
+@pytest.mark.parametrize("g", PLAN_GEOMS[:4] + [Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1),
+                                                Geometry(30, 8, 16, 256, 256, 3, 3, 1, 1)], ids=str)
 def test_backward_plans(g, stage):
     want_dx = g.sh == 1 and g.sw == 1
     if stage == 2 and not want_dx:
@@ -98,8 +102,18 @@ def test_backward_plans(g, stage):
     d = draw(g, "bwd", 43)
     res, devt = H.gpu_train(g, d)
     ob = H.oracle_backward_on_gpu_state(g, d, res, d["dy"], want_dx=want_dx)
+    ref = H.gpu_backward(g, devt, d["dy"], want_dx=want_dx)
     for plan in eligible(g, stage):
-        H.log(f"{'dgrad' if stage == 2 else 'wgrad'} plan {lib().cbr_plan_name(plan).decode()} {g}")
+        H.log(f"stage {stage} plan {lib().cbr_plan_name(plan).decode()} {g}")
         with forced(stage, plan):
             bw = H.gpu_backward(g, devt, d["dy"], want_dx=want_dx)
         H.check_backward(g, d, bw, ob, want_dx)
+        if stage == 4:
+            # without a dz output (the fused schedule forms dz inside the gradients, with
+            # the apply kernel's arithmetic, so the dz the gradients read is the one the
+            # default schedule stores)
+            with forced(stage, plan):
+                bn = H.gpu_backward(g, devt, d["dy"], want_dx=want_dx, dz_out=False)
+            for k in ("dgamma", "dbeta"):
+                np.testing.assert_array_equal(bn[k], ref[k], err_msg=k)
+            H.check_backward(g, d, dict(bn, dz=ref["dz"]), ob, want_dx)
