@@ -381,6 +381,37 @@ def main():
                                          kernel_entry("bn_stats_finalize", st2[1], 0, 0),
                                          kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0)]}
         del t2, z2, y2, m2, ws2
+        # the headline layer at other batch sizes: N = 32 (one GPU's share of 256 over 8)
+        # and N = 300 (more images than CUs); the persistent conv forced, as in the tests
+        import ctypes
+        lib = cbr._load()
+        for nb in (32, 300):
+            log(f"headline layer at N = {nb}")
+            wlb, db = draw_workload("s2_train", n=nb)
+            gb = wlb.geom
+            spb = shape_of(gb)
+            lib.cbr_set_plan_override(0, 1)
+            try:
+                tb = dict(x=to_bf16(db["x"]), w=to_bf16(db["w"]), ga=to_f32(db["gamma"]), be=to_f32(db["beta"]),
+                          rm=to_f32(db["run_mean"]), rv=to_f32(db["run_var"]))
+                zb = torch.empty((gb.n, gb.p, gb.q, gb.k), dtype=torch.int16, device=dev)
+                yb = torch.empty_like(zb)
+                mb = torch.empty(cbr.cbr_mask_words(spb), dtype=torch.int32, device=dev)
+                vb = [torch.empty(gb.k, device=dev) for _ in range(4)]
+                wsb = torch.empty(cbr.cbr_workspace_bytes(spb, cbr.CBR_OP_TRAIN), dtype=torch.uint8, device=dev)
+
+                def nb_step(events):
+                    cbr.cbr_forward_train(spb, tb["x"], tb["w"], tb["ga"], tb["be"], tb["rm"], tb["rv"], wlb.eps,
+                                          wlb.momentum, zb, yb, mb, vb[0], vb[1], vb[2], vb[3], wsb, events=events)
+
+                msb, stb, _ = timed(nb_step, 6, steps, 5)
+            finally:
+                lib.cbr_set_plan_override(0, 0)
+            aux[f"train_s2_n{nb}"] = {"workload": f"train forward N{nb} 56x56 C64->K64 3x3 (persistent conv)",
+                                      "ms": round(msb, 5), "conv_ms": round(stb[0], 5),
+                                      "images_per_ms": round(nb / msb, 2),
+                                      "conv_images_per_ms": round(nb / stb[0], 2)}
+            del tb, zb, yb, mb, wsb
         out["aux"] = aux
 
     # ---------------- on-box peaks: streaming copy and a large bf16 matmul ----------------

@@ -105,11 +105,12 @@ def _sp(shape):
 _E_VALUE = 7   # CBR_E_VALUE: the binding reports unusable tensors with it
 
 
-def _ptr(t, itemsize, name, where):
+def _ptr(t, itemsize, name, where, numel=None):
     """Device address of tensor t, after checking that the library can read it as the
     dense array of itemsize-byte elements that include/cbr.h describes: a CUDA (HIP)
-    tensor, contiguous in its own layout, with that element size.  An integer is taken
-    as a raw device address; None stays NULL."""
+    tensor, contiguous in its own layout, with that element size and at least numel
+    elements (the count the call's shape implies, when known).  An integer is taken as a
+    raw device address; None stays NULL."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -120,7 +121,21 @@ def _ptr(t, itemsize, name, where):
         raise CbrError(_E_VALUE, where, f"{name} is not contiguous (the library reads dense NHWC/KRSC arrays)")
     if t.element_size() != itemsize:
         raise CbrError(_E_VALUE, where, f"{name} has {t.element_size()}-byte elements, expected {itemsize}")
+    if numel is not None and t.numel() < numel:
+        raise CbrError(_E_VALUE, where, f"{name} holds {t.numel()} elements, the shape needs {numel}")
     return t.data_ptr()
+
+
+def _extents(shape):
+    """Element counts of a call's arrays for shape: x (NHWC), w (KRSC), out (NPQK: z, y,
+    dy, dz), k (per-channel vectors), mask (32-bit words).  All None when the library
+    rejects the shape: it then reports the shape's own error."""
+    p, q = ctypes.c_int32(), ctypes.c_int32()
+    if _load().cbr_output_hw(_sp(shape), ctypes.byref(p), ctypes.byref(q)) != 0:
+        return dict.fromkeys(("x", "w", "out", "k", "mask"))
+    s = shape
+    return dict(x=s.n * s.h * s.w * s.c, w=s.k * s.r * s.s * s.c, out=s.n * p.value * q.value * s.k, k=s.k,
+                mask=cbr_mask_words(shape))
 
 
 def _ws(workspace, where):
@@ -177,12 +192,14 @@ def cbr_forward_train(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, mo
                       workspace, stream=None, events=None):
     f = "cbr_forward_train"
     ws, nbytes = _ws(workspace, f)
-    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(gamma, 4, "gamma", f),
-            _ptr(beta, 4, "beta", f), _ptr(run_mean_in, 4, "run_mean_in", f), _ptr(run_var_in, 4, "run_var_in", f),
-            float(eps), float(momentum), _ptr(z, 2, "z", f), _ptr(y, 2, "y", f), _ptr(relu_mask, 4, "relu_mask", f),
-            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f),
-            _ptr(run_mean_out, 4, "run_mean_out", f), _ptr(run_var_out, 4, "run_var_out", f), ws, nbytes,
-            _stream(stream))
+    e = _extents(shape)
+    args = (_sp(shape), _ptr(x, 2, "x", f, e["x"]), _ptr(w, 2, "w", f, e["w"]), _ptr(gamma, 4, "gamma", f, e["k"]),
+            _ptr(beta, 4, "beta", f, e["k"]), _ptr(run_mean_in, 4, "run_mean_in", f, e["k"]),
+            _ptr(run_var_in, 4, "run_var_in", f, e["k"]), float(eps), float(momentum), _ptr(z, 2, "z", f, e["out"]),
+            _ptr(y, 2, "y", f, e["out"]), _ptr(relu_mask, 4, "relu_mask", f, e["mask"]),
+            _ptr(saved_mean, 4, "saved_mean", f, e["k"]), _ptr(saved_invstd, 4, "saved_invstd", f, e["k"]),
+            _ptr(run_mean_out, 4, "run_mean_out", f, e["k"]), _ptr(run_var_out, 4, "run_var_out", f, e["k"]),
+            ws, nbytes, _stream(stream))
     if events is None:
         _check(_load().cbr_forward_train(*args), f)
     else:
@@ -192,11 +209,14 @@ def cbr_forward_train(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, mo
 def cbr_forward_train_noalloc(shape, x, w, gamma, beta, run_mean_in, run_var_in, eps, momentum,
                               z, y, relu_mask, saved_mean, saved_invstd, run_mean_out, run_var_out, stream=None):
     f = "cbr_forward_train_noalloc"
-    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(gamma, 4, "gamma", f),
-            _ptr(beta, 4, "beta", f), _ptr(run_mean_in, 4, "run_mean_in", f), _ptr(run_var_in, 4, "run_var_in", f),
-            float(eps), float(momentum), _ptr(z, 2, "z", f), _ptr(y, 2, "y", f), _ptr(relu_mask, 4, "relu_mask", f),
-            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f),
-            _ptr(run_mean_out, 4, "run_mean_out", f), _ptr(run_var_out, 4, "run_var_out", f), _stream(stream))
+    e = _extents(shape)
+    args = (_sp(shape), _ptr(x, 2, "x", f, e["x"]), _ptr(w, 2, "w", f, e["w"]), _ptr(gamma, 4, "gamma", f, e["k"]),
+            _ptr(beta, 4, "beta", f, e["k"]), _ptr(run_mean_in, 4, "run_mean_in", f, e["k"]),
+            _ptr(run_var_in, 4, "run_var_in", f, e["k"]), float(eps), float(momentum), _ptr(z, 2, "z", f, e["out"]),
+            _ptr(y, 2, "y", f, e["out"]), _ptr(relu_mask, 4, "relu_mask", f, e["mask"]),
+            _ptr(saved_mean, 4, "saved_mean", f, e["k"]), _ptr(saved_invstd, 4, "saved_invstd", f, e["k"]),
+            _ptr(run_mean_out, 4, "run_mean_out", f, e["k"]), _ptr(run_var_out, 4, "run_var_out", f, e["k"]),
+            _stream(stream))
     _check(_load().cbr_forward_train_noalloc(*args), f)
 
 
@@ -204,9 +224,12 @@ def cbr_forward_infer(shape, x, w, conv_bias, gamma, beta, run_mean, run_var, ep
                       workspace, stream=None, events=None):
     f = "cbr_forward_infer"
     ws, nbytes = _ws(workspace, f)
-    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(conv_bias, 4, "conv_bias", f),
-            _ptr(gamma, 4, "gamma", f), _ptr(beta, 4, "beta", f), _ptr(run_mean, 4, "run_mean", f),
-            _ptr(run_var, 4, "run_var", f), float(eps), _ptr(y, 2, "y", f), ws, nbytes, _stream(stream))
+    e = _extents(shape)
+    args = (_sp(shape), _ptr(x, 2, "x", f, e["x"]), _ptr(w, 2, "w", f, e["w"]),
+            _ptr(conv_bias, 4, "conv_bias", f, e["k"]), _ptr(gamma, 4, "gamma", f, e["k"]),
+            _ptr(beta, 4, "beta", f, e["k"]), _ptr(run_mean, 4, "run_mean", f, e["k"]),
+            _ptr(run_var, 4, "run_var", f, e["k"]), float(eps), _ptr(y, 2, "y", f, e["out"]), ws, nbytes,
+            _stream(stream))
     if events is None:
         _check(_load().cbr_forward_infer(*args), f)
     else:
@@ -217,11 +240,13 @@ def cbr_backward(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd,
                  dz, dgamma, dbeta, dw, dx, workspace, stream=None, events=None):
     f = "cbr_backward"
     ws, nbytes = _ws(workspace, f)
-    args = (_sp(shape), _ptr(x, 2, "x", f), _ptr(w, 2, "w", f), _ptr(z, 2, "z", f),
-            _ptr(relu_mask, 4, "relu_mask", f), _ptr(dy, 2, "dy", f), _ptr(gamma, 4, "gamma", f),
-            _ptr(saved_mean, 4, "saved_mean", f), _ptr(saved_invstd, 4, "saved_invstd", f), _ptr(dz, 2, "dz", f),
-            _ptr(dgamma, 4, "dgamma", f), _ptr(dbeta, 4, "dbeta", f), _ptr(dw, 4, "dw", f), _ptr(dx, 2, "dx", f),
-            ws, nbytes, _stream(stream))
+    e = _extents(shape)
+    args = (_sp(shape), _ptr(x, 2, "x", f, e["x"]), _ptr(w, 2, "w", f, e["w"]), _ptr(z, 2, "z", f, e["out"]),
+            _ptr(relu_mask, 4, "relu_mask", f, e["mask"]), _ptr(dy, 2, "dy", f, e["out"]),
+            _ptr(gamma, 4, "gamma", f, e["k"]), _ptr(saved_mean, 4, "saved_mean", f, e["k"]),
+            _ptr(saved_invstd, 4, "saved_invstd", f, e["k"]), _ptr(dz, 2, "dz", f, e["out"]),
+            _ptr(dgamma, 4, "dgamma", f, e["k"]), _ptr(dbeta, 4, "dbeta", f, e["k"]), _ptr(dw, 4, "dw", f, e["w"]),
+            _ptr(dx, 2, "dx", f, e["x"]), ws, nbytes, _stream(stream))
     if events is None:
         _check(_load().cbr_backward(*args), f)
     else:
@@ -229,8 +254,9 @@ def cbr_backward(shape, x, w, z, relu_mask, dy, gamma, saved_mean, saved_invstd,
 
 
 def _conv_bias(name, shape, x, w, bias, y, stream, events):
-    args = (_sp(shape), _ptr(x, 2, "x", name), _ptr(w, 2, "w", name), _ptr(bias, 4, "bias", name),
-            _ptr(y, 2, "y", name), _stream(stream))
+    e = _extents(shape)
+    args = (_sp(shape), _ptr(x, 2, "x", name, e["x"]), _ptr(w, 2, "w", name, e["w"]),
+            _ptr(bias, 4, "bias", name, e["k"]), _ptr(y, 2, "y", name, e["out"]), _stream(stream))
     if events is None:
         _check(getattr(_load(), name)(*args), name)
     else:

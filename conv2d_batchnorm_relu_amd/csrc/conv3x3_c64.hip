@@ -1,11 +1,13 @@
 // conv3x3_c64.hip -- persistent 3x3 / stride 1 / pad 1 convolution with 64 input and 64
 // output channels (the CBR page's N=256, 56x56, 64-channel workload), fused with the
-// per-channel sum and sum of squares of its output (the conv + genstats step of the CBR
-// page's training forward, section 4.1).
+// per-channel statistics of its output (the conv + genstats step of the CBR page's
+// training forward, section 4.1).
 //
-// One 512-thread workgroup per compute unit (two waves per SIMD) walks whole images in
-// steps of SP = 256 output pixels (8 blocks of 32) in NHWC order, regardless of where
-// image rows begin, so that every SIMD has exactly two pixel blocks per full step.
+// Each image is cut into steps of SP = 256 output pixels (8 blocks of 32) in NHWC order,
+// regardless of where image rows begin, so that every SIMD has exactly two pixel blocks
+// per full step.  One 512-thread workgroup per compute unit (two waves per SIMD) walks a
+// contiguous range of the batch's steps (at most 256 ranges of near-equal length), so
+// the grid fills the chip for any batch size and ranges may begin inside an image.
 //   - Wave w computes output channels 32j .. 32j + 31, j = w / 4, and keeps that half of
 //     the filter, 32 x 576 bf16, in registers (36 MFMA operand fragments, 144 VGPRs), so
 //     LDS only serves input pixels.  Waves w and w + 4 share a SIMD and the same pixel
@@ -260,7 +262,12 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     const uint32_t mW = p.mW;
     const int HW = H * W;
     const int spi = (HW + SP - 1) / SP;                       // steps per image
-    const int nimg = (p.N - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    // This workgroup's steps: a contiguous range [t0, t1) of the N * spi steps of the batch
+    // in order (step s of image n is step n * spi + s), spread evenly over the grid, so
+    // every CU has work whatever N is and ranges may start inside an image.
+    const long tot = (long)p.N * spi;
+    const int t0 = (int)(tot * blockIdx.x / gridDim.x), t1 = (int)(tot * (blockIdx.x + 1) / gridDim.x);
+    const int n_first = t0 / spi, s_first = t0 - n_first * spi;
     const int hi = lane >> 5;                                 // k-half of the MFMA operands
     const int l32 = lane & 31;
     const int ipr = W / 8;                                    // 8-pixel load instructions per row
@@ -328,17 +335,21 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     // the staging buffers).  Load c gathers chunk c of all 64 rows (lane r), so the
     // fragment reads below are conflict-free.  Fragment t of lane (l32, hi) is output
     // channel 32j + l32, tap t / 4, input channels 16 (t % 4) + 8 hi .. + 7: chunk
-    // 8 (t / 4) + 2 (t % 4) + hi.  Meanwhile the first image's first rows stream into
-    // slots 0 .. rows0 - 1.
-    const int F = rows0 * SLOT;
+    // 8 (t / 4) + 2 (t % 4) + hi.  When the range starts at an image's first step, that
+    // step's rows stream into slots 0 .. rows0 - 1 meanwhile, and the filter sits past
+    // them; a range starting inside an image stages the filter at the start of LDS first
+    // and its first step's rows once the filter is in registers.
+    const bool at_start = s_first == 0;
+    const int F = at_start ? rows0 * SLOT : 0;
     for (int c = wave; c < 72; c += NW)
         __builtin_amdgcn_global_load_lds((const void *)(p.w + ((size_t)lane * 72 + c) * 8), (lds_u8 *)lds + F + c * 1024,
                                          16, 0, 0);
-    for (int c = tid; c < rows0 * 16; c += NT) {
+    const int zrows = at_start ? rows0 : 0;   // slots whose padding columns are zeroed now
+    for (int c = tid; c < zrows * 16; c += NT) {
         const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
         *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
     }
-    if (nimg > 0) stage_rows(blockIdx.x, -1, rows0);
+    if (at_start && t1 > t0) stage_rows(n_first, -1, rows0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     bf16x8 wf[KSTEPS];
@@ -349,9 +360,17 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     __syncthreads();   // the filter area is free again
     // The padding columns of the other slots zeroed (the k-loops' row loads fill the
     // other columns).
-    for (int c = rows0 * 16 + tid; c < NSLOT * 16; c += NT) {
+    for (int c = zrows * 16 + tid; c < NSLOT * 16; c += NT) {
         const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
         *(u32x4 *)(lds + slot * SLOT + col * PXB + (c & 7) * 16) = u32x4{0, 0, 0, 0};
+    }
+    if (!at_start) {
+        // input rows ofr - 1 .. olr + 1 of the first step's first and last output rows
+        const int a = s_first * SP, npix = min(SP, HW - a);
+        const int ofr = div_w(a, mW), olr = div_w(a + npix - 1, mW);
+        stage_rows(n_first, ofr - 1, olr - ofr + 3);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     // Per-lane running statistics (layout: see epilogue).
@@ -371,134 +390,136 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     constexpr int DMA_T0 = 6;                                 // k-step of the first row load
     static_assert(DMA_T0 + LPW <= KSTEPS, "the row loads fit in one k-loop");
     static_assert(2 * 4 * NSIMD * 1024 == STG_BYTES, "two halves of runs cover a step");
-    for (int img = 0; img < nimg; ++img) {
-        const int n = (int)blockIdx.x + img * (int)gridDim.x;
-        if (img > 0) {
-            // A new image: every wave is past the last step's reads; restage its first rows.
+    int n = n_first, s = s_first;   // image and step within it of step t
+    for (int t = t0; t < t1; ++t, ++s) {
+        if (s == spi) {
+            // The next image: every wave is past the last step's reads; restage its first
+            // rows.
+            ++n;
+            s = 0;
             stage_rows(n, -1, rows0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        for (int s = 0; s < spi; ++s) {
-            // Opaque per-step copy of the lane id: lane-derived addresses are recomputed
-            // each step instead of being hoisted into registers held through the k-loops.
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int l32s = ln & 31, his = ln >> 5;
-            const int a = s * SP;                               // first pixel of the step
-            const int npix = min(SP, HW - a);
-            const int nblk = (npix + 31) >> 5;                  // <= 8
-            const int nb = (simd < nblk) + (simd + NSIMD < nblk);
-            const bool full = npix == 32 * nblk;                // every pixel block complete
-            const int ofr = div_w(a, mW);                       // first output row of the step
-            const int olr = div_w(a + npix - 1, mW);            // last output row
-            const int fslot = ofr % NSLOT;                      // slot of input row ofr - 1
-            // The next step's new input rows olr + 2 .. olr1 + 1 (none after the image's
-            // last step) stream into their slots: load gi of them (row olr + 2 + gi / ipr,
-            // pixels 8 (gi % ipr) ..) goes to wave gi % 8 at k-step DMA_T0 + gi / 8.  The
-            // rows below H are contiguous in x, so load gi reads bytes 1024 gi .. of them;
-            // row H (the bottom padding) is written as zeros.
-            int nload = 0, nmem = 0;
-            if (s + 1 < spi) {
-                const int a1 = a + SP;
-                const int olr1 = div_w(a1 + min(SP, HW - a1) - 1, mW);
-                nload = (olr1 - olr) * ipr;
-                nmem = max(0, min(olr1, H - 2) - olr) * ipr;
-            }
-            const int slot_a = (olr + 3) % NSLOT;                // slot of input row olr + 2
-            const uint16_t *const xa = p.x + ((size_t)n * H + olr + 2) * W * HC;
-            auto row_part = [&](auto tc, int lt) {
-                constexpr int t = decltype(tc)::value - DMA_T0;
-                const int gi = wave + NW * t;                   // wave-uniform
-                if (gi < nload) {
-                    const int ri = div_w(8 * gi, mW);
-                    const int k = gi - ri * ipr;
-                    int sl = slot_a + ri;
-                    if (sl >= NSLOT) sl -= NSLOT;
-                    const int dst = sl * SLOT + (1 + 8 * k) * PXB;
-                    if (gi < nmem) {
-                        // lane l: pixel 8k + l/8, position l % 8, which holds channel chunk
-                        // (l % 8) ^ perm(1 + 8k + l/8) ^ row_flip(h)
-                        //   = (l % 8) ^ ((1 + l/8) / 2) ^ 4 (k % 2) ^ row_flip(h)
-                        const int l8 = lt >> 3;
-                        const int off = (l8 * HC + (((lt & 7) ^ ((1 + l8) >> 1)) << 3)) ^
-                                        (((k & 1) << 5) ^ (row_flip(olr + 2 + ri, ipr) << 3));
-                        __builtin_amdgcn_global_load_lds((const void *)(xa + gi * 512 + off), (lds_u8 *)lds + dst,
-                                                         16, 0, 0);
-                    } else {
-                        *(u32x4 *)(lds + dst + lt * 16) = u32x4{0, 0, 0, 0};
-                    }
-                }
-            };
-            const int cbuf = pbuf ^ 1;
-            uint8_t *const stg = stg0 + cbuf * STG_BYTES;
-            // The previous step's z: channel half 0's waves store the first half of its
-            // runs, the others the second half.
-            load_staged(prev, pbuf, j, ln);
-            if (nb == 0) {   // only in an image's last step (no row loads): no k-loop
-                staged_wait(prev);
-                for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
-            }
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                if (bb >= nb) break;
-                const int px = 32 * (simd + NSIMD * bb) + l32s;   // pixel within the step
-                const bool use = px < npix;
-                const int pi = a + (use ? px : 0);
-                const int pr = div_w(pi, mW);
-                const int q = pi - pr * W;
-                BlockAddr ba;
-#pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    int sl = fslot + (pr - ofr) + r;            // slot of input row pr + r - 1
-                    if (sl >= NSLOT) sl -= NSLOT;
-                    ba.rb[r] = (int)lbase + sl * SLOT + q * PXB;
-                }
-#pragma unroll
-                for (int sx = 0; sx < 3; ++sx) {
-                    // rows pr - 1 and pr + 1 share a flip; row pr's differs when W / 8 is odd
-                    ba.cx[0][sx] = (his ^ perm(q + sx) ^ row_flip(pr - 1, ipr)) << 4;
-                    ba.cx[1][sx] = ba.cx[0][sx] ^ ((ipr & 1) << 6);
-                }
-
-                f32x16 acc;
-                if (bb == 0) {
-                    // k-steps 2..5: this wave's half of the previous step's z runs (its LDS
-                    // reads have landed by then); 6 .. 6 + LPW - 1: the row loads
-                    auto side = [&](auto tc) {
-                        constexpr int T = decltype(tc)::value;
-                        // an opaque lane id per k-step keeps each instruction's address
-                        // computation at its k-step instead of in registers held from the start
-                        int lt = ln;
-                        asm volatile("" : "+v"(lt));
-                        if constexpr (T >= 2 && T < 6) {
-                            store_staged(prev, j, T - 2, lt);
-                        } else if constexpr (T >= DMA_T0 && T < DMA_T0 + LPW) {
-                            row_part(tc, lt);
-                        }
-                    };
-                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
-                } else {
-                    auto side = [](auto) {};
-                    KLoop<decltype(side)>{wf, ba, acc, side}.run();
-                }
-                if (full)
-                    epilogue<false>(acc, use, true, first, stg, px, j, his, c, s1, s2, cnt);
-                else
-                    epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, his, c, s1, s2, cnt);
-                first = false;
-            }
-
-            // The staged rows must have landed before any wave reads them: wait for this
-            // wave's loads, then the barrier publishes every wave's.  The barrier also
-            // frees the slots this step read for the steps after it, and publishes this
-            // step's staged z.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            prev.nq = npix / 8;
-            prev.zr = make_rsrc(p.z + ((size_t)n * HW + a) * HK, npix * HK * 2);
-            pbuf = cbuf;
+        const bool more = t + 1 < t1 && s + 1 < spi;   // the range's next step is in this image
+        // Opaque per-step copy of the lane id: lane-derived addresses are recomputed
+        // each step instead of being hoisted into registers held through the k-loops.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l32s = ln & 31, his = ln >> 5;
+        const int a = s * SP;                               // first pixel of the step
+        const int npix = min(SP, HW - a);
+        const int nblk = (npix + 31) >> 5;                  // <= 8
+        const int nb = (simd < nblk) + (simd + NSIMD < nblk);
+        const bool full = npix == 32 * nblk;                // every pixel block complete
+        const int ofr = div_w(a, mW);                       // first output row of the step
+        const int olr = div_w(a + npix - 1, mW);            // last output row
+        const int fslot = ofr % NSLOT;                      // slot of input row ofr - 1
+        // The next step's new input rows olr + 2 .. olr1 + 1 (none after the image's
+        // last step) stream into their slots: load gi of them (row olr + 2 + gi / ipr,
+        // pixels 8 (gi % ipr) ..) goes to wave gi % 8 at k-step DMA_T0 + gi / 8.  The
+        // rows below H are contiguous in x, so load gi reads bytes 1024 gi .. of them;
+        // row H (the bottom padding) is written as zeros.
+        int nload = 0, nmem = 0;
+        if (more) {
+            const int a1 = a + SP;
+            const int olr1 = div_w(a1 + min(SP, HW - a1) - 1, mW);
+            nload = (olr1 - olr) * ipr;
+            nmem = max(0, min(olr1, H - 2) - olr) * ipr;
         }
+        const int slot_a = (olr + 3) % NSLOT;                // slot of input row olr + 2
+        const uint16_t *const xa = p.x + ((size_t)n * H + olr + 2) * W * HC;
+        auto row_part = [&](auto tc, int lt) {
+            constexpr int t = decltype(tc)::value - DMA_T0;
+            const int gi = wave + NW * t;                   // wave-uniform
+            if (gi < nload) {
+                const int ri = div_w(8 * gi, mW);
+                const int k = gi - ri * ipr;
+                int sl = slot_a + ri;
+                if (sl >= NSLOT) sl -= NSLOT;
+                const int dst = sl * SLOT + (1 + 8 * k) * PXB;
+                if (gi < nmem) {
+                    // lane l: pixel 8k + l/8, position l % 8, which holds channel chunk
+                    // (l % 8) ^ perm(1 + 8k + l/8) ^ row_flip(h)
+                    //   = (l % 8) ^ ((1 + l/8) / 2) ^ 4 (k % 2) ^ row_flip(h)
+                    const int l8 = lt >> 3;
+                    const int off = (l8 * HC + (((lt & 7) ^ ((1 + l8) >> 1)) << 3)) ^
+                                    (((k & 1) << 5) ^ (row_flip(olr + 2 + ri, ipr) << 3));
+                    __builtin_amdgcn_global_load_lds((const void *)(xa + gi * 512 + off), (lds_u8 *)lds + dst,
+                                                     16, 0, 0);
+                } else {
+                    *(u32x4 *)(lds + dst + lt * 16) = u32x4{0, 0, 0, 0};
+                }
+            }
+        };
+        const int cbuf = pbuf ^ 1;
+        uint8_t *const stg = stg0 + cbuf * STG_BYTES;
+        // The previous step's z: channel half 0's waves store the first half of its
+        // runs, the others the second half.
+        load_staged(prev, pbuf, j, ln);
+        if (nb == 0) {   // only in an image's last step (no row loads): no k-loop
+            staged_wait(prev);
+            for (int k = 0; k < 4; ++k) store_staged(prev, j, k, ln);
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            if (bb >= nb) break;
+            const int px = 32 * (simd + NSIMD * bb) + l32s;   // pixel within the step
+            const bool use = px < npix;
+            const int pi = a + (use ? px : 0);
+            const int pr = div_w(pi, mW);
+            const int q = pi - pr * W;
+            BlockAddr ba;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                int sl = fslot + (pr - ofr) + r;            // slot of input row pr + r - 1
+                if (sl >= NSLOT) sl -= NSLOT;
+                ba.rb[r] = (int)lbase + sl * SLOT + q * PXB;
+            }
+#pragma unroll
+            for (int sx = 0; sx < 3; ++sx) {
+                // rows pr - 1 and pr + 1 share a flip; row pr's differs when W / 8 is odd
+                ba.cx[0][sx] = (his ^ perm(q + sx) ^ row_flip(pr - 1, ipr)) << 4;
+                ba.cx[1][sx] = ba.cx[0][sx] ^ ((ipr & 1) << 6);
+            }
+
+            f32x16 acc;
+            if (bb == 0) {
+                // k-steps 2..5: this wave's half of the previous step's z runs (its LDS
+                // reads have landed by then); 6 .. 6 + LPW - 1: the row loads
+                auto side = [&](auto tc) {
+                    constexpr int T = decltype(tc)::value;
+                    // an opaque lane id per k-step keeps each instruction's address
+                    // computation at its k-step instead of in registers held from the start
+                    int lt = ln;
+                    asm volatile("" : "+v"(lt));
+                    if constexpr (T >= 2 && T < 6) {
+                        store_staged(prev, j, T - 2, lt);
+                    } else if constexpr (T >= DMA_T0 && T < DMA_T0 + LPW) {
+                        row_part(tc, lt);
+                    }
+                };
+                KLoop<decltype(side)>{wf, ba, acc, side}.run();
+            } else {
+                auto side = [](auto) {};
+                KLoop<decltype(side)>{wf, ba, acc, side}.run();
+            }
+            if (full)
+                epilogue<false>(acc, use, true, first, stg, px, j, his, c, s1, s2, cnt);
+            else
+                epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, his, c, s1, s2, cnt);
+            first = false;
+        }
+
+        // The staged rows must have landed before any wave reads them: wait for this
+        // wave's loads, then the barrier publishes every wave's.  The barrier also
+        // frees the slots this step read for the steps after it, and publishes this
+        // step's staged z.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        prev.nq = npix / 8;
+        prev.zr = make_rsrc(p.z + ((size_t)n * HW + a) * HK, npix * HK * 2);
+        pbuf = cbuf;
     }
     load_staged(prev, pbuf, j, lane);
     staged_wait(prev);
@@ -603,7 +624,11 @@ bool halo_eligible(const ConvGeom &g)
     return hw * g.W < (1ull << 32) && halo_lds_bytes(g) <= (size_t)HALO_MAX_LDS;
 }
 
-int halo_grid(const ConvGeom &g) { return std::min(g.N, HALO_MAX_GRID); }
+int halo_grid(const ConvGeom &g)
+{
+    const long steps = (long)g.N * ((g.H * g.W + SP - 1) / SP);
+    return (int)std::min<long>(steps, HALO_MAX_GRID);
+}
 
 hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
                                     float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)

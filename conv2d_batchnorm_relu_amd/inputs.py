@@ -147,7 +147,9 @@ def draw(geom: Geometry, call: str, seed: int, bf16: bool = True) -> dict:
 
 
 def draw_workload(name: str, n: int | None = None) -> tuple[Workload, dict]:
-    """Inputs of a named workload (optionally with fewer images, same recipe)."""
+    """Inputs of a named workload, optionally with another batch size (same recipe).  The
+    returned workload's geometry is the one the inputs were drawn for."""
     wl = WORKLOADS[name]
-    geom = wl.geom if n is None else wl.geom.with_n(n)
-    return wl, draw(geom, wl.call, wl.seed, wl.bf16)
+    if n is not None:
+        wl = replace(wl, geom=wl.geom.with_n(n))
+    return wl, draw(wl.geom, wl.call, wl.seed, wl.bf16)

@@ -237,3 +237,33 @@ def test_plan_interface(lib):
         sp = cbr.make_shape(n, h, w, c, k, r, s, sh, ph, stride_w=sw, pad_w=pw)
         assert L.cbr_plan_eligible(ctypes.byref(sp), st, plan) == 1, row
         assert L.cbr_plan_of(ctypes.byref(sp), st) == plan, row
+
+
+@pytest.mark.gpu
+def test_binding_rejects_short_tensors():
+    """A tensor with fewer elements than the call's shape implies (say, inputs drawn for a
+    smaller batch) is refused by the binding before any kernel could run past its end."""
+    import torch
+    sp = cbr.make_shape(4, 8, 8, 64, 64, 3, 3, 1, 1)
+    dev = "cuda"
+    x_short = torch.zeros(2, 8, 8, 64, dtype=torch.bfloat16, device=dev)
+    w = torch.zeros(64, 3, 3, 64, dtype=torch.bfloat16, device=dev)
+    b = torch.zeros(64, device=dev)
+    y = torch.empty(4, 8, 8, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(cbr.CbrError, match="x holds 8192 elements, the shape needs 16384"):
+        cbr.cbr_conv2d_bias_relu(sp, x_short, w, b, y)
+    x = torch.zeros(4, 8, 8, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(cbr.CbrError, match="y holds"):
+        cbr.cbr_conv2d_bias(sp, x, w, b, y[:2])
+    with pytest.raises(cbr.CbrError, match="bias holds"):
+        cbr.cbr_conv2d_bias(sp, x, w, b[:32], y)
+
+
+def test_draw_workload_geometry_matches_inputs():
+    """A workload drawn at another batch size reports the geometry its inputs have."""
+    from conv2d_batchnorm_relu_amd.inputs import draw_workload
+    wl, d = draw_workload("s2_train", n=3)
+    g = wl.geom
+    assert g.n == 3 and d["x"].shape == (3, g.h, g.w, g.c) and d["w"].shape == (g.k, g.r, g.s, g.c)
+    wl0, _ = draw_workload("tiny")
+    assert wl0.geom.n == 2

@@ -43,8 +43,10 @@ def test_train_forward_small(g):
 
 
 # The persistent 3x3 / 64-channel kernel (W a multiple of 8, 8..56; steps of 256 pixels
-# that start anywhere in a row): partial last steps and pixel blocks, steps spanning up
-# to 33 rows, several images per workgroup (N > 256), images smaller than one step.
+# that start anywhere in a row; each workgroup a contiguous range of the batch's steps):
+# partial last steps and pixel blocks, steps spanning up to 33 rows, ranges that start
+# inside an image (batches of fewer steps than workgroups) and that cross image ends
+# (N > 256), images smaller than one step.
 # The 64-channel 3x3 shapes it does not take (W % 8 != 0) run the generic conv.
 HALO_GEOMS = [
     Geometry(2, 12, 16, 64, 64, 3, 3, 1, 1),     # one step of 6 blocks
@@ -62,6 +64,27 @@ HALO_GEOMS = [
     Geometry(2, 12, 12, 64, 64, 3, 3, 1, 1),     # generic conv (W % 8 != 0)
     Geometry(300, 5, 7, 64, 64, 3, 3, 1, 1),     # generic conv, N > 256
 ]
+
+
+@pytest.mark.parametrize("n", [32, 300])
+def test_train_forward_headline_shape_other_batches(n):
+    """The persistent 3x3 kernel on the 56x56x64 layer at N = 32 (256 ranges of one or two
+    steps, most starting inside an image) and N = 300 (ranges crossing image ends), forced
+    whatever the plan table prefers, every output against the oracle."""
+    import ctypes
+    import conv2d_batchnorm_relu_amd as cbr
+    wl, d = draw_workload("s2_train", n=n)
+    g = wl.geom
+    lib = cbr._load()
+    assert lib.cbr_set_plan_override(0, 1) == 0
+    try:
+        assert lib.cbr_plan_of(ctypes.byref(H.cshape(g)), 0) == 1
+        H.log(f"persistent 3x3, N = {n}")
+        res, _ = H.gpu_train(g, d, wl.eps, wl.momentum)
+    finally:
+        lib.cbr_set_plan_override(0, 0)
+    ora = H.oracle_train(g, d, wl.eps, wl.momentum)
+    H.check_train(g, d, res, ora, wl.eps, wl.momentum)
 
 
 @pytest.mark.parametrize("g", HALO_GEOMS, ids=str)
