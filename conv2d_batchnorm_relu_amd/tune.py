@@ -10,6 +10,7 @@ fastest.  It writes the table that csrc/cbr_plan.cpp compiles in (cbr_tune_table
 and a markdown summary of every timing.  Rebuild the library after replacing the table.
 
     python -m conv2d_batchnorm_relu_amd.tune --out-dir gpurun_out/tune [--batch 32 256] [--reps 10]
+        [--match '56x56 64->64 3x3'] [--stages 0 1]
 
 A stage's plans are compared by the time of the whole call that contains the stage (the
 training forward, the conv + bias + ReLU call, the backward), measured with HIP events
@@ -58,10 +59,13 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--out-dir", default="gpurun_out/tune")
     ap.add_argument("--batch", type=int, nargs="+", default=[32, 256])
-    ap.add_argument("--vgg-batch", type=int, nargs="+", default=[32])
+    ap.add_argument("--vgg-batch", type=int, nargs="*", default=[32])
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--max-elems", type=int, default=1 << 29, help="skip layers whose tensors exceed this")
+    ap.add_argument("--match", default=None,
+                    help="only layers whose label 'HxW C->K RxS/stride' contains this text (e.g. '56x56 64->64 3x3')")
+    ap.add_argument("--stages", type=int, nargs="+", default=list(STAGES), help="stages to time (0..4)")
     args = ap.parse_args(argv)
 
     import torch
@@ -79,6 +83,8 @@ def main(argv=None):
     layers += [("vgg16bn", n, L) for n in args.vgg_batch for L in vgg16_layers()]
     entries, report = [], []
     for net, n, (h, w, c, k, r, s, st, pd) in layers:
+        if args.match is not None and args.match not in f"{h}x{w} {c}->{k} {r}x{s}/{st}":
+            continue
         sp = cbr.make_shape(n, h, w, c, k, r, s, st, pd)
         try:
             P, Q = cbr.cbr_output_hw(sp)
@@ -123,6 +129,8 @@ def main(argv=None):
         run_train(None)   # a z, mask and saved statistics for the backward
         torch.cuda.synchronize()
         for stage, sname in STAGES.items():
+            if stage not in args.stages:
+                continue
             if stage in (2, 4) and st != 1:
                 continue   # the data gradient needs stride 1
             cands = [p for p in PLANS if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
