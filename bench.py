@@ -15,7 +15,6 @@ the host as a reported baseline (unless --no-cpu-baseline).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -74,42 +73,53 @@ def bwd_bytes(g):
     return {"bn_backward": (z + mask + z) * 2 + z, "conv_wgrad": z + x + dw, "conv_dgrad": z + w + x}
 
 
-def kernel_entry(name, ms, nbytes, flops):
+def kernel_entry(name, ms, nbytes, flops, prof=None):
+    """Timing of one stage against its algorithmic bytes and flops; prof = (workload,
+    kernel-name prefixes) names the stage's kernels in the committed counter summary,
+    whose measured HBM bytes per call are added while the library's sources are the ones
+    the counters were taken on."""
     t = ms * 1e-3
     gbs = nbytes / t / 1e9 if t > 0 else 0.0
     tfl = flops / t / 1e12 if t > 0 else 0.0
-    return {"kernel": name, "ms": round(ms, 5), "gbps": round(gbs, 1), "tflops": round(tfl, 2),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
-            "bytes": int(nbytes), "flops": int(flops)}
+    e = {"kernel": name, "ms": round(ms, 5), "gbps": round(gbs, 1), "tflops": round(tfl, 2),
+         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+         "bytes": int(nbytes), "flops": int(flops)}
+    if prof is not None:
+        c = counted_stage(*prof)
+        if c is not None:
+            e["traffic"] = c["traffic"]
+            e["traffic_over_algorithmic"] = round(c["traffic"] / nbytes, 3) if nbytes else None
+            if c["mfma_util_pct"] is not None:
+                e["mfma_util_pct_counter"] = c["mfma_util_pct"]
+    return e
 
 
-# Sources of the persistent 3x3 kernel: measured HBM traffic stored under profiles/ is
-# reported only while these files are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv3x3_c64_stats_n256_56x56.json")
-KERNEL_SOURCES = ["conv2d_batchnorm_relu_amd/csrc/conv3x3_c64.hip", "conv2d_batchnorm_relu_amd/csrc/cbr_common.h",
-                  "conv2d_batchnorm_relu_amd/csrc/cbr_launch.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bench_workloads.json")
+_counters = None
 
 
-def sources_digest():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def measured_traffic():
-    """HBM bytes per launch of the persistent conv from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factors), or None when the
-    summary is missing or was taken on other kernel sources."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+def counted_stage(workload, prefixes):
+    """Measured HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE) per call of a stage: the sum
+    over the workload's kernels whose names start with one of prefixes and that ran once
+    per call (the profiled run makes 5 calls); also the MFMA utilisation of its busiest
+    kernel.  None when the summary is missing or was taken on other library sources."""
+    global _counters
+    if _counters is None:
+        try:
+            with open(COUNTERS_FILE) as f:
+                _counters = json.load(f)
+        except (OSError, ValueError):
+            _counters = {}
+        from conv2d_batchnorm_relu_amd.profile_summary import sources_sha256
+        if _counters.get("sources_sha256") != sources_sha256():
+            _counters = {}
+    rows = [r for r in _counters.get("workloads", {}).get(workload, [])
+            if r["kernel"].startswith(tuple(prefixes)) and r["dispatches"] == 5]
+    if not rows or any(r["fetch_bytes"] is None or r["write_bytes"] is None for r in rows):
         return None
-    if t.get("sources_sha256") != sources_digest():
-        return None
-    return int(t["traffic_bytes_per_launch"])
+    util = [r["mfma_util_pct"] for r in rows if r["mfma_util_pct"]]
+    return {"traffic": int(sum(r["fetch_bytes"] + r["write_bytes"] for r in rows)),
+            "mfma_util_pct": max(util) if util else None}
 
 
 def roofline_of(entry, traffic=None):
@@ -231,9 +241,11 @@ def main():
     ms, stages, per = timed(train_step, 6, args.steps, args.warmup)
     flops = conv_flops(g)
     kb = train_bytes(g)
-    kernels = [kernel_entry("conv3x3_c64_stats", stages[0], kb["conv_fprop_stats"], flops),
+    kernels = [kernel_entry("conv3x3_c64_stats", stages[0], kb["conv_fprop_stats"], flops,
+                            ("train_s2", ["conv3x3_c64_stats"])),
                kernel_entry("bn_stats_finalize", stages[1], 0, 0),
-               kernel_entry("bn_apply_relu_mask", stages[2], kb["bn_apply_relu_mask"], 0)]
+               kernel_entry("bn_apply_relu_mask", stages[2], kb["bn_apply_relu_mask"], 0,
+                            ("train_s2", ["bn_apply_relu_mask"]))]
     dominant = max(kernels, key=lambda e: e["ms"])
     total_bytes = sum(kb.values())
 
@@ -272,7 +284,7 @@ def main():
         "step_roofline_frac": round(total_bytes / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4),
         "bytes_per_step": int(total_bytes),
         "unfused_bytes": int(unfused_train_bytes(g)),
-        "roofline": roofline_of(dominant, measured_traffic() if dominant is kernels[0] else None),
+        "roofline": roofline_of(dominant, dominant.get("traffic")),
         "kernels": kernels,
         "kernel_ms_spread": {e["kernel"]: spread(v) for e, v in zip(kernels, per)},
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
@@ -301,9 +313,9 @@ def main():
         ib = infer_bytes(g4)
         aux["infer"] = {"workload": "infer N256 28x28 C128->K128 3x3 s1 p1 (conv bias)", "ms": round(ms4, 5),
                         "tflops": round(conv_flops(g4) / (ms4 * 1e-3) / 1e12, 2),
-                        "kernels": [kernel_entry("bn_fold", st4[0], ib["bn_fold"], 0),
+                        "kernels": [kernel_entry("bn_fold", st4[0], ib["bn_fold"], 0, ("infer_s3", ["bn_fold"])),
                                     kernel_entry("conv_fprop_bias_relu", st4[1], ib["conv_fprop_bias_relu"],
-                                                 conv_flops(g4))]}
+                                                 conv_flops(g4), ("infer_s3", ["conv_igemm", "conv_fprop"]))]}
         log("conv + bias + relu workload")
 
         def cbr_step(events):
@@ -313,7 +325,7 @@ def main():
         aux["conv_bias_relu"] = {"workload": "Conv2D + bias + ReLU, no BN: N256 28x28 C128->K128 3x3 s1 p1",
                                  "ms": round(ms4c, 5), "tflops": round(conv_flops(g4) / (ms4c * 1e-3) / 1e12, 2),
                                  "kernels": [kernel_entry("conv_bias_relu", st4c[0], ib["conv_fprop_bias_relu"],
-                                                          conv_flops(g4))]}
+                                                          conv_flops(g4), ("conv_bias_relu", ["conv_igemm", "conv_fprop"]))]}
         del t4
         log("backward workload")
         wl5, d5 = draw_workload("s4_bwd")
@@ -348,9 +360,11 @@ def main():
         f5 = conv_flops(g5)
         aux["backward"] = {"workload": "backward N256 14x14 C256->K256 3x3 s1 p1", "ms": round(ms5, 5),
                            "tflops": round(2 * f5 / (ms5 * 1e-3) / 1e12, 2),
-                           "kernels": [kernel_entry("bn_backward", st5[0], bb["bn_backward"], 0),
-                                       kernel_entry("conv_wgrad", st5[1], bb["conv_wgrad"], f5),
-                                       kernel_entry("conv_dgrad", st5[2], bb["conv_dgrad"], f5)]}
+                           "kernels": [kernel_entry("bn_backward", st5[0], bb["bn_backward"], 0, ("bwd_s4", ["bnbwd_"])),
+                                       kernel_entry("conv_wgrad", st5[1], bb["conv_wgrad"], f5,
+                                                    ("bwd_s4", ["conv_wgrad", "split_sum"])),
+                                       kernel_entry("conv_dgrad", st5[2], bb["conv_dgrad"], f5,
+                                                    ("bwd_s4", ["flip_weights", "conv_igemm", "conv_fprop"]))]}
         ms5f, st5f, _ = timed(fwd5, 6, steps, 5)
         aux["train_s4"] = {"workload": "train forward N256 14x14 C256->K256 3x3", "ms": round(ms5f, 5),
                            "tflops": round(f5 / (ms5f * 1e-3) / 1e12, 2)}
@@ -377,9 +391,11 @@ def main():
         aux["stem_train"] = {"workload": "train forward N64 224x224 C3->K64 7x7 s2 p3", "ms": round(ms2, 5),
                              "gbps": round(sum(kb2.values()) / (ms2 * 1e-3) / 1e9, 1),
                              "kernels": [kernel_entry("conv_fprop_stats(first layer)", st2[0],
-                                                      kb2["conv_fprop_stats"], conv_flops(g2)),
+                                                      kb2["conv_fprop_stats"], conv_flops(g2),
+                                                      ("train_stem", ["widen_filter", "conv_c3s2"])),
                                          kernel_entry("bn_stats_finalize", st2[1], 0, 0),
-                                         kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0)]}
+                                         kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0,
+                                                      ("train_stem", ["bn_apply_relu_mask"]))]}
         del t2, z2, y2, m2, ws2
         # the headline layer at other batch sizes: N = 32 (one GPU's share of 256 over 8)
         # and N = 300 (more images than CUs); the persistent conv forced, as in the tests
