@@ -96,13 +96,31 @@ __global__ __launch_bounds__(NT) void bn_fold_kernel(const uint16_t *__restrict_
                                                      float eps, int K, int Kg, uint16_t *__restrict__ wf,
                                                      float *__restrict__ bf)
 {
-    // block k folds output channel k: s_k once, then its Kg filter values
+    // block k folds output channel k: s_k once, then its Kg filter values (8 per 16-byte
+    // chunk when the rows are whole chunks; the row's first chunks are loaded before the
+    // scale's arithmetic, so the two latencies overlap)
     const int k = blockIdx.x;
-    const double sd = (double)gamma[k] / sqrt((double)rv[k] + (double)eps);
-    const float sf = (float)sd;
     const uint16_t *wk = w + (size_t)k * Kg;
     uint16_t *wfk = wf + (size_t)k * Kg;
-    for (int i = threadIdx.x; i < Kg; i += NT) wfk[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(wk[i]) * sf);
+    const bool vec = Kg % 8 == 0;
+    const int i0 = threadIdx.x;
+    u32x4 first = u32x4{0u, 0u, 0u, 0u};
+    if (vec && 8 * i0 < Kg) first = *(const u32x4 *)(wk + 8 * i0);
+    const double sd = (double)gamma[k] / sqrt((double)rv[k] + (double)eps);
+    const float sf = (float)sd;
+    if (vec) {
+        auto scale8 = [&](u32x4 v) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf16x2(bf16_bits_to_f32(v[e] & 0xffffu) * sf, bf16_bits_to_f32(v[e] >> 16) * sf);
+            return o;
+        };
+        if (8 * i0 < Kg) *(u32x4 *)(wfk + 8 * i0) = scale8(first);
+        for (int i = i0 + NT; 8 * i < Kg; i += NT) *(u32x4 *)(wfk + 8 * i) = scale8(*(const u32x4 *)(wk + 8 * i));
+    } else {
+        for (int i = threadIdx.x; i < Kg; i += NT) wfk[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(wk[i]) * sf);
+    }
     if (threadIdx.x == 0) {
         const double b = bias ? (double)bias[k] : 0.0;
         bf[k] = (float)((b - (double)rm[k]) * sd + (double)beta[k]);

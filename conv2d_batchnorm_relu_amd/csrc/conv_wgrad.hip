@@ -337,18 +337,28 @@ __global__ __launch_bounds__(NT) void split_sum_kernel(const float *__restrict__
 }
 
 // Filter of the data gradient as a forward convolution (stride 1):
-// wt[c][r'][s'][k] = w[k][R-1-r'][S-1-s'][c].
+// wt[c][r'][s'][k] = w[k][R-1-r'][S-1-s'][c].  Thread t makes the eight outputs of
+// k = 8 k8 .. 8 k8 + 7 at one (c, r', s'), t = ((k8 R + r') S + s') C + c: its eight
+// 2-byte reads are coalesced over the threads of consecutive c, and the outputs leave as
+// one 16-byte store (K % 8 == 0).  32-bit indices: filters hold far fewer than 2^31
+// elements.
 __global__ __launch_bounds__(NT) void flip_weights_kernel(const uint16_t *__restrict__ w, int K, int R, int S, int C,
                                                           uint16_t *__restrict__ wt)
 {
-    const long total = (long)K * R * S * C;
-    for (long i = (long)blockIdx.x * NT + threadIdx.x; i < total; i += (long)gridDim.x * NT) {
-        long t = i;
-        const int k = (int)(t % K); t /= K;
-        const int s = (int)(t % S); t /= S;
-        const int r = (int)(t % R); t /= R;
-        const int c = (int)t;
-        wt[i] = w[(((size_t)k * R + (R - 1 - r)) * S + (S - 1 - s)) * C + c];
+    const int total = (K / 8) * R * S * C;
+    const int rsc = R * S * C;
+    for (int t = blockIdx.x * NT + threadIdx.x; t < total; t += gridDim.x * NT) {
+        const int c = t % C;
+        int u = t / C;
+        const int s = u % S;
+        u /= S;
+        const int r = u % R, k8 = u / R;
+        const uint16_t *src = w + ((size_t)(8 * k8) * R + (R - 1 - r)) * S * C + (S - 1 - s) * C + c;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)src[(size_t)(2 * e) * rsc] | ((uint32_t)src[(size_t)(2 * e + 1) * rsc] << 16);
+        *(u32x4 *)(wt + (((size_t)c * R + r) * S + s) * K + 8 * k8) = u32x4{v[0], v[1], v[2], v[3]};
     }
 }
 
@@ -722,7 +732,7 @@ hipError_t launch_conv_wgrad_fused(const ConvGeom &g, const uint16_t *dy, const 
 hipError_t launch_flip_weights(int K, int R, int S, int C, const uint16_t *w, uint16_t *wt, hipStream_t st,
                                hipEvent_t e0, hipEvent_t e1)
 {
-    const long total = (long)K * R * S * C;
+    const long total = (long)(K / 8) * R * S * C;   // K % 8 == 0 (shape validation)
     const int blocks = (int)std::min<long>((total + NT - 1) / NT, 4096);
     return launch(flip_weights_kernel, dim3(blocks), dim3(NT), 0, st, e0, e1, w, K, R, S, C, wt);
 }
