@@ -41,21 +41,30 @@
 #include <hip/hip_ext.h>
 
 #include "cbr_launch.h"
+#include "cbr_persist.h"
 
 namespace cbr {
 namespace {
 
+using persist::f32x16;
+using persist::HK;
+using persist::lds_u8;
+using persist::make_rsrc;
+using persist::NSIMD;
+using persist::NT;
+using persist::NW;
+using persist::perm;
+using persist::SP;
+using persist::Staged;
+using persist::STATS_BYTES;
+using persist::STG_BYTES;
+using persist::u32x2;
+
 constexpr int HC = 64;                  // input channels
-constexpr int HK = 64;                  // output channels
-constexpr int SP = 256;                 // output pixels per step
-constexpr int PXB = HC * 2;             // bytes per staged pixel
-constexpr int NT = 512;                 // threads: 8 waves, two per SIMD
-constexpr int NW = NT / 64;
-constexpr int NSIMD = 4;
+constexpr int PXB = HC * 2;             // bytes per staged input pixel (and per z pixel)
+static_assert(PXB == persist::PXB, "input and output pixels have the same size");
 constexpr int MAXW = 56;
 constexpr int KSTEPS = 36;              // 9 taps x 4 chunks of 16 input channels
-constexpr int STG_BYTES = SP * PXB;     // one step's z, pixel-major
-constexpr int STATS_BYTES = NW * 4 * 17 * 4;    // final cross-lane combination area
 constexpr int FILTER_BYTES = HK * 72 * 16;    // the filter, staged once through LDS
 // Row loads per wave per step: a step adds at most ceil(SP / W) input rows of W / 8
 // loads each, i.e. at most SP / 8 + W / 8 <= 39 loads over the 8 waves.
@@ -73,15 +82,10 @@ struct HaloParams {
     uint32_t mW;           // ceil(2^32 / W): v / W == mulhi(v, mW) for v < 2^32 / W
 };
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
 __device__ __forceinline__ int div_w(int v, uint32_t mW) { return (int)__umulhi((uint32_t)v, mW); }
 
-// Chunk permutation of staged pixel u (of a z staging row, or of input row h together
-// with row_flip): channel chunk c is stored at position c ^ perm(u) (^ row_flip(h)).
-__device__ __forceinline__ int perm(int u) { return (u >> 1) & 7; }
+// Input pixels are permuted like staged z pixels (perm, with row_flip): channel chunk c
+// of pixel u of input row h is stored at position c ^ perm(u) ^ row_flip(h).
 
 // The input-row permutation continues across rows as if the rows were one run of pixels:
 // pixel u of row h is permuted like pixel u + (h + 1) W of one long row, i.e. by
@@ -90,11 +94,6 @@ __device__ __forceinline__ int perm(int u) { return (u >> 1) & 7; }
 // inside a row does; with a plain per-row permutation the two rows' positions repeat and
 // every read of such a block takes twice as long.
 __device__ __forceinline__ int row_flip(int h, int ipr) { return (((h + 1) * ipr) & 1) << 2; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
 
 // Per pixel block: LDS address of the lane's staged pixel q in the slot of tap row r
 // (rb[r]), and the lane's chunk permutation of pixels q + sx, pre-shifted and with the
@@ -181,75 +180,6 @@ struct KLoop {
         prefetch<0>();
         step<0>();
     }
-};
-
-// v_permlane16_swap exchanges the odd 16-lane rows of a with the even rows of b: after
-// it, lanes of even rows hold a of both pixels l and l + 16, lanes of odd rows b of
-// pixels l - 16 and l.  Lanes l and l ^ 16 hold the same channels, so a swap and an add
-// halve the registers a running per-channel sum needs.
-__device__ __forceinline__ void swap_rows(float &a, float &b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-
-// Statistics and staging of one pixel block.  The lane holds, for pixel l32 of the
-// block, channels 32j + 8g + 4hi + e in acc[4g + e] (32x32x16 layout: row
-// 8*(v/4) + 4*(l/32) + v%4).  After the swap, pair i (i = 4g + e, g < 2) of lane l holds
-// channel 32j + 8(g + 2 ((l / 16) % 2)) + 4hi + e of pixels l and l ^ 16 (in that order
-// in even 16-lane rows, the other way round in odd ones).  Running sums s1[i], s2[i] are
-// of the deviations d = z - c[i] from the lane's shift c[i], which the wave's first
-// block sets to the pair's first value (the shifted-data form of the one-pass variance:
-// deviations from a value of the channel do not cancel when its mean is far from zero);
-// cnt counts the values summed.  With MASKED, values of pixels past the step (own: !use,
-// partner: !use_p) are left out.  The bf16 results go to staging row px (16-byte chunk
-// c of a row at position c ^ perm(px)).
-template <bool MASKED>
-__device__ __forceinline__ void epilogue(const f32x16 &acc, bool use, bool use_p, bool first, uint8_t *stg, int px,
-                                         int j, int hi, float (&c)[8], float (&s1)[8], float (&s2)[8], float &cnt)
-{
-    float v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = acc[k];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        *(u32x2 *)(stg + px * PXB + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
-            u32x2{pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-    const bool even = (px & 16) == 0;
-    const bool ua = even ? use : use_p, ub = even ? use_p : use;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) swap_rows(v[i], v[i + 8]);
-    if (first) {
-        // a pixel past the step holds the conv output of the step's first pixel: a value
-        // of the channel all the same
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = v[i];
-    }
-    // both values of pair i are the same channel: their deviations go to s1, their
-    // squares to s2 (two fused multiply-adds)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float a = v[i] - c[i], b = v[i + 8] - c[i];
-        if constexpr (MASKED) {
-            a = ua ? a : 0.f;
-            b = ub ? b : 0.f;
-        }
-        s1[i] += a + b;
-        s2[i] = fmaf(b, b, fmaf(a, a, s2[i]));
-    }
-    if constexpr (MASKED)
-        cnt += (float)ua + (float)ub;
-    else
-        cnt += 2.f;
-}
-
-// A staged step awaiting its stores: d[k] holds run k of the half being stored (a run is
-// 1 KB, pixels 8q .. 8q + 7); nq runs in all, bound for zr.
-struct Staged {
-    u32x4 d[4];
-    int nq;                          // 0: nothing staged
-    __amdgpu_buffer_rsrc_t zr;
 };
 
 __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
@@ -505,9 +435,9 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
                 KLoop<decltype(side)>{wf, ba, acc, side}.run();
             }
             if (full)
-                epilogue<false>(acc, use, true, first, stg, px, j, his, c, s1, s2, cnt);
+                persist::epilogue<false>(acc, use, true, first, stg, px, j, his, c, s1, s2, cnt);
             else
-                epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, his, c, s1, s2, cnt);
+                persist::epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, his, c, s1, s2, cnt);
             first = false;
         }
 
@@ -526,74 +456,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     for (int k = 0; k < 4; ++k) store_staged(prev, j, k, lane);
     __syncthreads();   // every wave is done with the staging buffers and the ring
 
-    // Combination of the lanes' statistics (count n, mean = c + s1/n, M2 = s2 - s1^2/n)
-    // by the law of total variance, mean = sum n_l mean_l / n, M2 = sum [M2_l + n_l
-    // (mean_l - mean)^2]: first over the 16 lanes of a 16-lane row, which hold the same
-    // channels (butterflies of lane shuffles, fp32; the two operands of every addition
-    // are the same at both lanes, so the sums are identical across the row), then over
-    // the 4 waves of a channel half in fp64, one thread per channel.  st[w][r][f]: wave w,
-    // 16-lane row r, f = 0: count, 1 + i: mean of pair i, 9 + i: M2 of pair i.
-    float *st = (float *)lds;             // [NW][4][17]
-    {
-        const float rc = cnt > 0.f ? 1.f / cnt : 0.f;
-        float ml[8], q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ml[i] = c[i] + s1[i] * rc;
-            q[i] = fmaxf(s2[i] - s1[i] * s1[i] * rc, 0.f);
-        }
-        auto rowsum = [](float v) {
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
-            return v;
-        };
-        const float nr = rowsum(cnt);
-        const float rn = nr > 0.f ? 1.f / nr : 0.f;
-        float mr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mr[i] = rowsum(cnt * ml[i]) * rn;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float d = ml[i] - mr[i];
-            q[i] = rowsum(fmaf(cnt * d, d, q[i]));
-        }
-        if ((lane & 15) == 0) {
-            float *e = st + (wave * 4 + (lane >> 4)) * 17;
-            e[0] = nr;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[1 + i] = mr[i];
-                e[9 + i] = q[i];
-            }
-        }
-    }
-    __syncthreads();
-    if (tid < HK) {
-        // channel k = 32j + 8g + 4h + e lives in waves 4j .. 4j + 3, 16-lane row 2h + g/2,
-        // pair i = 4 (g % 2) + e
-        const int k = tid;
-        const int jk = k >> 5, g = (k >> 3) & 3, h = (k >> 2) & 1, e = k & 3;
-        const int r = 2 * h + (g >> 1), i = 4 * (g & 1) + e;
-        double n = 0.0, sm = 0.0;
-#pragma unroll
-        for (int w = 0; w < NSIMD; ++w) {
-            const float *en = st + ((4 * jk + w) * 4 + r) * 17;
-            n += (double)en[0];
-            sm += (double)en[0] * (double)en[1 + i];
-        }
-        const double mean = n > 0.0 ? sm / n : 0.0;
-        double m2 = 0.0;
-#pragma unroll
-        for (int w = 0; w < NSIMD; ++w) {
-            const float *en = st + ((4 * jk + w) * 4 + r) * 17;
-            const double d = (double)en[1 + i] - mean;
-            m2 += (double)en[9 + i] + (double)en[0] * d * d;
-        }
-        float *row = p.partials + (size_t)blockIdx.x * 2 * HK;
-        row[k] = (float)mean;
-        row[HK + k] = (float)m2;
-        if (k == 0) p.partials[(size_t)gridDim.x * 2 * HK + blockIdx.x] = (float)n;
-    }
+    persist::store_stat_row(lds, c, s1, s2, cnt, p.partials, blockIdx.x, gridDim.x);
 }
 
 }  // namespace

@@ -1,303 +1,335 @@
-// conv_c3s2.hip -- first-layer convolution (3 input channels, stride 2, up to 7x8
-// taps, 64 output channels) fused with the per-channel sum and sum of squares of its
-// output: the training forward's conv + genstats step (CBR page, section 4.1) for the
-// network's input layer (the CBR page's first-layer special case, section 5.3, is the
-// backward's skipped data gradient; this is its forward).
+// conv_c3s2.hip -- persistent first-layer convolution (3 input channels, stride 2, up
+// to 7x8 taps, 64 output channels) fused with the per-channel statistics of its output:
+// the training forward's conv + genstats step (CBR page, section 4.1) for the network's
+// input layer.
 //
-// With 3 channels a pixel is 6 bytes, so the generic implicit GEMM gathers element by
-// element.  Here each workgroup owns TP = 4 output rows of one image.  It stages the
-// 2*(TP-1) + R input rows it needs in LDS with every pixel widened to 4 channels (8
-// bytes, the fourth zero) and zero columns on both sides, and the filter widened to
-// [64][R][8][4] (taps s >= S and channel 3 zero).  The reduction is then ordered
-// (r, s, c) with s and c innermost: for a fixed tap row r, the 16 values of one MFMA
-// k-step are four consecutive input pixels x 4 channels, and because the stride is 2,
-// the 8 values a lane needs for output column q are one aligned 16-byte LDS read at
-// pixel 2q + s0.  Consecutive output columns read consecutive 16-byte chunks, so the
-// reads are conflict-free.
-//
-// GEMM mapping: v_mfma_f32_32x32x16_bf16, filter as A (32 output channels), pixels as
-// B (32 output pixels), 2*R k-steps (R*32 reduction values, S*3 of every 32 live).
-// Four waves: wave w owns channel block w/2 and pixel blocks 7*(w%2) .. 7*(w%2)+6 of the
-// band's 14 (4 rows x 112 columns for the 224x224 stem).  Two workgroups share a CU,
-// so one's staging overlaps the other's MFMAs.
+// With 3 channels a pixel is 6 bytes, so a generic implicit GEMM would gather element by
+// element.  Here input pixels are widened to 4 channels (8 bytes, the fourth zero) and
+// the filter to [64][R][8][4] (taps s >= S and channel 3 zero), so that for a fixed tap
+// row r the 16 values of one MFMA k-step are four consecutive input pixels x 4 channels
+// and, with stride 2, the 8 values a lane needs for output column q are one aligned
+// 16-byte LDS read at widened pixel 2q + s0 (2R k-steps, R*32 reduction slots of which
+// R*S*3 are live).
+// The schedule is that of the persistent 3x3 kernel (conv3x3_c64.hip):
+//   - One 512-thread workgroup per CU walks a contiguous range of the batch's steps of
+//     SP = 256 output pixels (8 blocks of 32, NHWC order, starting anywhere in a row);
+//     SIMD s takes blocks s and s + 4, the two waves of a SIMD the two channel halves.
+//   - Wave w keeps its half of the widened filter in registers (2R fragments).
+//   - LDS holds a ring of widened input rows: row h (-ph <= h) in slot (h + ph) % nslot,
+//     zero columns on both sides; rows outside the image are zero rows.  While a step
+//     computes, each thread holds one 8-pixel piece of the rows the next step adds (three
+//     16-byte loads issued at the step's start); after the step's k-loops it widens the
+//     piece into its slot, which no wave of the step reads.
+//   - z goes through two LDS staging buffers and leaves, during the next step, as 1 KB
+//     runs of whole 128-byte pixel rows; the statistics are kept per lane as shifted sums
+//     and combined once at the end into one (count, mean, M2) row per workgroup.
 #include "cbr_launch.h"
+#include "cbr_persist.h"
 
 namespace cbr {
 namespace {
 
-constexpr int NT = 256;
-constexpr int TP = 4;          // output rows per workgroup
-constexpr int KOUT = 64;       // output channels
-constexpr int UPW = 7;         // pixel blocks per wave
-constexpr int NBLK = 2 * UPW;  // pixel blocks per band (TP * Q <= 32 * NBLK)
+using namespace persist;
 
-struct C3Params {
+constexpr int KMAX = 14;   // k-steps: two per filter row, R <= 7
+
+struct C3PParams {
     const uint16_t *x;      // N x H x W x 3
     const uint16_t *wexp;   // 64 x R x 8 x 4 (zero-padded filter)
     uint16_t *z;            // N x P x Q x 64
     float *partials;        // [gridDim.x][2][64] means and M2, then [gridDim.x] counts
     int N, H, W, R, ph, pw, P, Q;
-    int bands;              // ceil(P / TP)
-    int LW;                 // staged pixels per input row (zero columns included)
-    int RB;                 // bytes per staged input row
-    int WRB;                // bytes per staged filter row
+    int slot_bytes;         // LW * 8: widened pixels per staged row, zero columns included
+    int nslot;              // ring slots
+    uint32_t mQ, mG;        // ceil(2^32 / Q), ceil(2^32 / (W / 8)): multiply-high divisions
 };
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+// v / d for the divisor d whose magic m = ceil(2^32 / d) (truncated to 32 bits) is given:
+// exact for v < 2^32 / d; d = 1 has m = 0 and returns v.
+__device__ __forceinline__ int div_m(int v, uint32_t m) { return m ? (int)__umulhi((uint32_t)v, m) : v; }
 
-// Chunk permutation of the z staging rows: 16-byte chunk c of pixel px sits at position
-// c ^ perm(px), so consecutive pixels' chunks spread over the LDS banks.
-__device__ __forceinline__ int perm(int px) { return (px >> 1) & 7; }
+// Workgroup barrier over LDS only: every wave's LDS operations have completed when any
+// wave passes it; global stores stay in flight (nothing in the kernel reads what they
+// write, and their data was read from registers when they were issued).  The memory
+// clobbers keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Widened filter [64][R][8][4] <- KRSC [64][R][S][3], zeros elsewhere.
-__global__ __launch_bounds__(NT) void widen_filter_c3_kernel(const uint16_t *__restrict__ w, int R, int S,
+__global__ __launch_bounds__(256) void widen_filter_c3_kernel(const uint16_t *__restrict__ w, int R, int S,
                                                              uint16_t *__restrict__ wexp)
 {
-    const int total = KOUT * R * 32;
-    for (int i = blockIdx.x * NT + threadIdx.x; i < total; i += gridDim.x * NT) {
+    const int total = HK * R * 32;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
         const int c = i & 3, s = (i >> 2) & 7, kr = i >> 5;          // kr = k*R + r
         wexp[i] = (c < 3 && s < S) ? w[((size_t)kr * S + s) * 3 + c] : (uint16_t)0;
     }
 }
 
-__global__ __launch_bounds__(NT, 2) void conv_c3s2_stats_kernel(C3Params p)
+// Eight pixels of an input row: 48 bytes of x (three 16-byte loads).
+struct Piece {
+    u32x4 a, b, d;
+};
+
+__global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int NR = 2 * (TP - 1) + p.R;              // staged input rows
-    uint8_t *wl = lds;                              // KOUT x WRB
-    uint8_t *xl = lds + KOUT * p.WRB;               // NR x RB
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = blockIdx.x / p.bands, band = blockIdx.x - n * p.bands;
-    const int p0 = band * TP;
-    const int h0 = 2 * p0 - p.ph;                   // input row of staged row 0
-    const int W = p.W, Q = p.Q;
-
-    // The staging loops index with lane bit fields, not divisions: an integer division
-    // by a run-time value is some forty vector instructions.
-    // Filter: R*4 <= 32 16-byte chunks per output channel; lane bits 0..4 pick the chunk.
-    {
-        const int cpr = p.R * 4, ch = tid & 31;
-        if (ch < cpr)
-            for (int k = tid >> 5; k < KOUT; k += NT / 32)
-                *(u32x4 *)(wl + k * p.WRB + ch * 16) = ((const u32x4 *)p.wexp)[k * cpr + ch];
-    }
-    // Input rows.  Zero: rows outside the image, and the columns left and right of the
-    // image (staged pixel j holds input column j - pw; at most 16 of them per row).  Image
-    // pixels: groups of 8 (48 bytes = three 16-byte loads), widened to 8 bytes each.
-    const int gpr = W / 8;                          // pixel groups per row
-    const int npad = p.LW - W;                      // zero columns per row, <= 16
-    for (int i = tid >> 4; i < NR; i += NT / 16) {
-        const int h = h0 + i, c = tid & 15;
-        if (h >= 0 && h < p.H) {
-            if (c < npad) {
-                const int j = c < p.pw ? c : W + c;
-                *(u32x2 *)(xl + i * p.RB + j * 8) = u32x2{0u, 0u};
-            }
-        } else {
-            for (int j = c; j < p.LW; j += 16) *(u32x2 *)(xl + i * p.RB + j * 8) = u32x2{0u, 0u};
-        }
-    }
-    for (int i = tid >> 5; i < NR; i += NT / 32) {
-        const int h = h0 + i;
-        if (h < 0 || h >= p.H) continue;
-        for (int gi = tid & 31; gi < gpr; gi += 32) {
-        const u32x4 *src = (const u32x4 *)(p.x + (((size_t)n * p.H + h) * W + 8 * gi) * 3);
-        const u32x4 a = src[0], b = src[1], d = src[2];
-        const uint32_t v[12] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], d[0], d[1], d[2], d[3]};
-        uint8_t *dst = xl + i * p.RB + (p.pw + 8 * gi) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // bf16 values 3e, 3e+1, 3e+2 of the group; value t is half t%2 of word t/2.
-            auto half = [&](int t) { return (v[t >> 1] >> (16 * (t & 1))) & 0xffffu; };
-            const uint32_t lo = half(3 * e) | (half(3 * e + 1) << 16);
-            *(u32x2 *)(dst + e * 8) = u32x2{lo, half(3 * e + 2)};
-        }
-        }
-    }
-    __syncthreads();
-
-    // Wave's channel block and pixel blocks; per-block staged-pixel base of its lane.
-    const int j = wave >> 1, blk0 = UPW * (wave & 1);
+    const int simd = wave & (NSIMD - 1), j = wave >> 2;
     const int hi = lane >> 5, l32 = lane & 31;
-    const int wa = (32 * j + l32) * p.WRB + hi * 16;
-    int xa[UPW];
-    bool valid[UPW];
-    const float invQ = 1.0f / (float)Q;
-#pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-        const int pi = 32 * (blk0 + u) + l32;           // pixel within the band
-        int pr = (int)((float)pi * invQ);               // pi / Q, corrected below
-        pr -= pr * Q > pi;
-        pr += (pr + 1) * Q <= pi;
-        const int q = pi - pr * Q;
-        valid[u] = pr < TP && p0 + pr < p.P;
-        xa[u] = valid[u] ? KOUT * p.WRB + 2 * pr * p.RB + 2 * q * 8 + hi * 16 : KOUT * p.WRB;
-    }
+    const int H = p.H, W = p.W, Q = p.Q, R = p.R, SB = p.slot_bytes, NSLOT = p.nslot;
+    const int PQ = p.P * Q;
+    const int spi = (PQ + SP - 1) / SP;                       // steps per image
+    // This workgroup's steps: a contiguous range [t0, t1) of the N * spi steps of the batch
+    // (step s of image n is step n * spi + s), spread evenly over the grid.
+    const long tot = (long)p.N * spi;
+    const int t0 = (int)(tot * blockIdx.x / gridDim.x), t1 = (int)(tot * (blockIdx.x + 1) / gridDim.x);
+    const int gpr = W / 8;                                    // 8-pixel pieces per input row
+    const int nks = 2 * R;
+    uint8_t *const stg0 = lds + NSLOT * SB;                   // two z staging buffers
 
-    // k-step t: tap row r = t/2, taps s = 4*(t%2) .. +3 (lane half hi: two of them).
-    const int nks = 2 * p.R;
-    f32x16 acc[UPW];
+    // Filter fragment t (k-step t): lane (l32, hi) holds output channel 32j + l32, tap row
+    // t / 2, taps 4 (t % 2) + 2 hi and + 1, four channels each: 16 bytes of wexp.
+    bf16x8 wf[KMAX];
 #pragma unroll
-    for (int u = 0; u < UPW; ++u)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[u][v] = 0.f;
-    bf16x8 af[2], bf[2][UPW];
-    auto rd = [&](int t, int b) {
-        const int r = t >> 1, hf = t & 1;
-        af[b] = *(const bf16x8 *)(lds + wa + r * 64 + hf * 32);
-#pragma unroll
-        for (int u = 0; u < UPW; ++u) bf[b][u] = *(const bf16x8 *)(lds + xa[u] + r * p.RB + hf * 32);
-    };
-    rd(0, 0);
-    for (int t = 0; t < nks; t += 2) {
-        rd(t + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < UPW; ++u)
-            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[0][u], acc[u], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + 2 < nks) rd(t + 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < UPW; ++u)
-            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf[1][u], acc[u], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int t = 0; t < KMAX; ++t)
+        wf[t] = t < nks ? *(const bf16x8 *)(p.wexp + ((size_t)(32 * j + l32) * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi)
+                        : bf16x8{};
 
-    // Epilogue: lane holds, for pixel l32 of each block, channels 32j + 8g + 4hi + e in
-    // acc[u][4g + e].  Per-lane statistics; z goes through LDS (the staged rows and the
-    // filter are free once every wave is past the barrier) into pixel-major order, 16-byte
-    // chunk c of band pixel px at (c ^ perm(px)) << 4, and leaves as 1 KB runs of whole
-    // 128-byte pixel rows: storing straight from the MFMA layout touches 32 cache lines per
-    // instruction with 16 bytes each, which the memory pipeline processes line by line.
-    // Statistics, first pass: per-lane channel sums over the valid pixels.
-    float s1[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s1[g][e] = 0.f;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-        if (!valid[u]) continue;
-        const int px = 32 * (blk0 + u) + l32;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float a0 = acc[u][4 * g], a1 = acc[u][4 * g + 1];
-            const float a2 = acc[u][4 * g + 2], a3 = acc[u][4 * g + 3];
-            *(u32x2 *)(lds + px * 128 + (((4 * j + g) ^ perm(px)) << 4) + 8 * hi) =
-                u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-            s1[g][0] += a0;
-            s1[g][1] += a1;
-            s1[g][2] += a2;
-            s1[g][3] += a3;
+    // Piece g of input row h of image n (zeros outside the image), and its widened store
+    // into the row's slot: pixel u of the row at byte (pw + u) * 8 of the slot.
+    auto load_piece = [&](int n, int h, int g) {
+        Piece r;
+        if (h >= 0 && h < H) {
+            const u32x4 *src = (const u32x4 *)(p.x + (((size_t)n * H + h) * W + 8 * g) * 3);
+            r.a = src[0];
+            r.b = src[1];
+            r.d = src[2];
+        } else {
+            r.a = r.b = r.d = u32x4{0u, 0u, 0u, 0u};
         }
-    }
-    __syncthreads();
-    // The band's rows are contiguous in z (NHWC): npx pixels from pixel (n, p0, 0).
-    const int npx = min(TP, p.P - p0) * Q;
+        return r;
+    };
+    auto store_piece = [&](int h, int g, const Piece &r) {
+        uint8_t *dst = lds + ((h + p.ph) % NSLOT) * SB + (p.pw + 8 * g) * 8;
+        const uint32_t v[12] = {r.a[0], r.a[1], r.a[2], r.a[3], r.b[0], r.b[1], r.b[2], r.b[3], r.d[0], r.d[1], r.d[2], r.d[3]};
+        // bf16 value t of the piece is half t % 2 of word t / 2; pixel e is values 3e .. 3e + 2
+        auto half = [&](int t) { return (v[t >> 1] >> (16 * (t & 1))) & 0xffffu; };
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *(u32x2 *)(dst + e * 8) = u32x2{half(3 * e) | (half(3 * e + 1) << 16), half(3 * e + 2)};
+    };
+    // Rows h0 .. h0 + nrows - 1 of image n, every piece, loaded and stored in place.
+    auto stage_rows = [&](int n, int h0, int nrows) {
+        for (int i = tid; i < nrows * gpr; i += NT) {
+            const int ri = div_m(i, p.mG);
+            const int g = i - ri * gpr;
+            store_piece(h0 + ri, g, load_piece(n, h0 + ri, g));
+        }
+    };
+
+    // The zero columns of every slot (left of the image and right of it, up to the last
+    // widened pixel a read can reach).
     {
-        const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
-            p.z + ((size_t)n * p.P + p0) * Q * KOUT, 0, npx * KOUT * 2, 0x00020000);
-        // sc1 without nt: measured, the z lines then still sit in the last-level cache for
-        // the normalisation pass that reads them next, and the stores run as fast.
-        constexpr int Z_POLICY = 16;
-        for (int q = wave; q < (npx + 7) / 8; q += NT / 64) {
-            const int px = 8 * q + (lane >> 3);   // runs past npx: the buffer drops the store
-            const u32x4 v = *(const u32x4 *)(lds + px * 128 + (((lane & 7) ^ perm(px)) << 4));
-            __builtin_amdgcn_raw_buffer_store_b128(v, zr, q * 1024 + lane * 16, 0, Z_POLICY);
+        const int lw = SB / 8, nz = lw - W;
+        for (int i = tid; i < NSLOT * nz; i += NT) {
+            const int sl = i / nz, c = i - sl * nz;
+            const int col = c < p.pw ? c : W + c;
+            *(u32x2 *)(lds + sl * SB + col * 8) = u32x2{0u, 0u};
         }
     }
+    int n = t0 / spi, s = t0 - n * spi;                      // image and step of step t
+    if (t1 > t0) {
+        // the first step's input rows 2 ofr - ph .. 2 olr - ph + R - 1
+        const int a = s * SP, npix = min(SP, PQ - a);
+        const int ofr = div_m(a, p.mQ), olr = div_m(a + npix - 1, p.mQ);
+        stage_rows(n, 2 * ofr - p.ph, 2 * (olr - ofr) + R);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    // Cross-lane reductions through LDS, once every wave has read its z runs:
-    // st[f][tid], f = 4*g + e for channel 32j + 8g + 4hi + e.  Thread (f, jj, h) of the
-    // first 128 sums the 64 lanes of channel block jj with hi == h (waves 2jj and 2jj + 1
-    // x 32 lanes) in a fixed order.
-    __syncthreads();
-    float *st = (float *)lds;            // 16 x NT floats = 16 KB
-    float *bmean = st + 16 * NT;         // the band's 64 channel means
-    auto reduce = [&](int f, int jj, int h) {
-        float a = 0.f;
+    float c[8], s1[8], s2[8], cnt = 0.f;
 #pragma unroll
-        for (int w = 2 * jj; w < 2 * jj + 2; ++w) {
-            const f32x4 *row = (const f32x4 *)(st + f * NT + 64 * w + 32 * h);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const f32x4 q = row[i];
-                a += (q[0] + q[1]) + (q[2] + q[3]);
+    for (int i = 0; i < 8; ++i) {
+        c[i] = 0.f;
+        s1[i] = 0.f;
+        s2[i] = 0.f;
+    }
+    bool first = true;   // wave-uniform: the wave's first pixel block sets the shifts
+    Staged prev;         // the previous step, staged in buffer pbuf
+    prev.nq = 0;
+    prev.zr = make_rsrc(p.z, 0);   // nothing staged yet: every store is dropped
+    int pbuf = 1;
+    // sc1 without nt: the z lines then still sit in the last-level cache for the
+    // normalisation pass that reads them next.
+    constexpr int Z_POLICY = 16;
+
+    for (int t = t0; t < t1; ++t, ++s) {
+        if (s == spi) {
+            // The next image: every wave is past the last step's reads; stage the rows of
+            // its first step.
+            ++n;
+            s = 0;
+            const int olr0 = div_m(min(SP, PQ) - 1, p.mQ);
+            stage_rows(n, -p.ph, 2 * olr0 + R);
+            lds_barrier();
+        }
+        const int a = s * SP;                                   // first pixel of the step
+        const int npix = min(SP, PQ - a);
+        const int nblk = (npix + 31) >> 5;
+        const int nb = (simd < nblk) + (simd + NSIMD < nblk);
+        const bool full = npix == 32 * nblk;
+        const int ofr = div_m(a, p.mQ), olr = div_m(a + npix - 1, p.mQ);
+        // The rows the next step of the range adds (none at an image's or the range's end):
+        // input rows 2 olr - ph + R .. 2 olr1 - ph + R - 1, at most one piece per thread.
+        Piece nx;
+        int nx_h = 0, nx_g = 0;
+        bool nx_on = false;
+        if (t + 1 < t1 && s + 1 < spi) {
+            const int a1 = a + SP;
+            const int olr1 = div_m(a1 + min(SP, PQ - a1) - 1, p.mQ);
+            if (tid < 2 * (olr1 - olr) * gpr) {
+                const int ri = div_m(tid, p.mG);
+                nx_g = tid - ri * gpr;
+                nx_h = 2 * olr - p.ph + R + ri;
+                nx = load_piece(n, nx_h, nx_g);
+                nx_on = true;
             }
         }
-        return a;
-    };
-    const int rf = tid >> 2, rjj = (tid >> 1) & 1, rh = tid & 1;      // reducing thread's role
-    const int rk = 32 * rjj + 8 * (rf >> 2) + 4 * rh + (rf & 3);      // its channel
+        // The previous step's z: channel half 0's waves store the first half of its runs,
+        // the others the second half.
+        if (prev.nq > 0) {
+            const uint8_t *sb = stg0 + pbuf * STG_BYTES;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st[(4 * g + e) * NT + tid] = s1[g][e];
-    __syncthreads();
-    if (tid < 64) bmean[rk] = reduce(rf, rjj, rh) / (float)npx;
-    __syncthreads();
-    // Second pass: squared deviations of the valid pixels from the band's means.
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const f32x4 m4 = *(const f32x4 *)(bmean + 32 * j + 8 * g + 4 * hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float s2 = 0.f;
-#pragma unroll
-            for (int u = 0; u < UPW; ++u) {
-                const float d = acc[u][4 * g + e] - m4[e];
-                s2 = valid[u] ? fmaf(d, d, s2) : s2;
+            for (int k = 0; k < 4; ++k) {
+                const int q = simd + NSIMD * (4 * j + k);
+                const int px = 8 * q + (lane >> 3);
+                prev.d[k] = *(const u32x4 *)(sb + px * PXB + (((lane & 7) ^ perm(px)) << 4));
             }
-            st[(4 * g + e) * NT + tid] = s2;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int q = simd + NSIMD * (4 * j + k);
+                __builtin_amdgcn_raw_buffer_store_b128(prev.d[k], prev.zr, q * 1024 + lane * 16, 0, Z_POLICY);
+            }
+        }
+        const int cbuf = pbuf ^ 1;
+        uint8_t *const stg = stg0 + cbuf * STG_BYTES;
+        // slot of input row 2 ofr - ph (tap row 0 of the step's first output row)
+        const int fslot = (2 * ofr) % NSLOT;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            if (bb >= nb) break;
+            const int px = 32 * (simd + NSIMD * bb) + l32;      // pixel within the step
+            const bool use = px < npix;
+            const int pi = a + (use ? px : 0);
+            const int pr = div_m(pi, p.mQ);
+            const int q = pi - pr * Q;
+            // tap row r of output row pr reads input row 2 pr - ph + r, in slot
+            // (2 pr + r) % nslot
+            int sl0 = fslot + 2 * (pr - ofr);
+            while (sl0 >= NSLOT) sl0 -= NSLOT;
+            const int colb = 16 * q + 16 * hi;
+            bf16x8 xf[KMAX];
+#pragma unroll
+            for (int tt = 0; tt < KMAX; ++tt) {
+                if (tt < nks) {
+                    int sl = sl0 + (tt >> 1);
+                    if (sl >= NSLOT) sl -= NSLOT;
+                    xf[tt] = *(const bf16x8 *)(lds + sl * SB + colb + 32 * (tt & 1));
+                }
+            }
+            f32x16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < KMAX; ++tt)
+                if (tt < nks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[tt], xf[tt], acc, 0, 0, 0);
+            if (full)
+                epilogue<false>(acc, use, true, first, stg, px, j, hi, c, s1, s2, cnt);
+            else
+                epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, hi, c, s1, s2, cnt);
+            first = false;
+        }
+        // The next step's rows into their slots (no wave of this step reads them).
+        if (nx_on) store_piece(nx_h, nx_g, nx);
+        // The barrier publishes the staged rows and this step's staged z, and frees the
+        // staging buffer the previous step's z was read from; the z stores run on.
+        lds_barrier();
+        prev.nq = (npix + 7) / 8;
+        prev.zr = make_rsrc(p.z + ((size_t)n * PQ + a) * HK, npix * HK * 2);
+        pbuf = cbuf;
+    }
+    if (prev.nq > 0) {
+        const uint8_t *sb = stg0 + pbuf * STG_BYTES;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = simd + NSIMD * (4 * j + k);
+            const int px = 8 * q + (lane >> 3);
+            prev.d[k] = *(const u32x4 *)(sb + px * PXB + (((lane & 7) ^ perm(px)) << 4));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = simd + NSIMD * (4 * j + k);
+            __builtin_amdgcn_raw_buffer_store_b128(prev.d[k], prev.zr, q * 1024 + lane * 16, 0, Z_POLICY);
         }
     }
-    __syncthreads();
-    if (tid < 64) {
-        float *row = p.partials + (size_t)blockIdx.x * 2 * KOUT;
-        row[rk] = bmean[rk];
-        row[KOUT + rk] = reduce(rf, rjj, rh);
-    }
-    if (tid == 0) p.partials[(size_t)gridDim.x * 2 * KOUT + blockIdx.x] = (float)npx;
+    lds_barrier();   // every wave is done with the staging buffers and the ring
+    store_stat_row(lds, c, s1, s2, cnt, p.partials, blockIdx.x, gridDim.x);
 }
 
-int c3_bands(const ConvGeom &g) { return (g.P + TP - 1) / TP; }
-int c3_lw(const ConvGeom &g) { return std::max(2 * (g.Q - 1) + 8, g.pw + g.W); }
+// Widened pixels per staged row: up to the last one a read reaches (2 (Q - 1) + 7) and
+// past the image's right edge, rounded up to even so that slots start on 16 bytes.
+int c3p_lw(const ConvGeom &g)
+{
+    const int lw = std::max(2 * (g.Q - 1) + 8, g.pw + g.W);
+    return lw + (lw & 1);
+}
+// Ring slots: the input rows of a step and the rows the next adds, 2 (olr(s + 1) - ofr(s))
+// + R, where the output rows of 2 SP consecutive pixels span at most (2 SP - 1) / Q + 2.
+int c3p_nslot(const ConvGeom &g) { return 2 * ((2 * SP - 1) / g.Q + 1) + g.R; }
 
 }  // namespace
 
 bool c3s2_eligible(const ConvGeom &g)
 {
-    // 14 pixel blocks of 32 must cover TP output rows; the filter row (R taps of 8 x 4)
-    // and the staged rows must fit LDS with two workgroups per CU.
-    return g.C == 3 && g.K == KOUT && g.sh == 2 && g.sw == 2 && g.R >= 1 && g.R <= 7 && g.S >= 1 && g.S <= 8 &&
-           g.W % 8 == 0 && TP * g.Q <= 32 * NBLK && (g.pw % 2) == 1 && c3_lw(g) - g.W <= 16 &&
-           c3s2_lds_bytes(g) <= 80 * 1024 &&
-           (size_t)g.N * g.P * g.Q * KOUT * 2 < 0x7fffffffu;
+    if (!(g.C == 3 && g.K == HK && g.sh == 2 && g.sw == 2 && g.R >= 1 && g.R <= 7 && g.S >= 1 && g.S <= 8 &&
+          g.W % 8 == 0 && g.ph >= 0 && g.pw >= 0 && g.P >= 1 && g.Q >= 1))
+        return false;
+    // zero columns left and right of the image: at most 16 per row
+    if (c3p_lw(g) - g.W > 16 || c3p_lw(g) < g.pw + g.W) return false;
+    // one piece per thread of the rows a step adds: 2 (SP / Q + 1) rows of W / 8 pieces
+    if (2 * (SP / g.Q + 1) * (g.W / 8) > NT) return false;
+    // the multiply-high divisions: pixel indices below 2^32 / Q
+    if ((uint64_t)((size_t)g.P * g.Q + SP) * g.Q >= (1ull << 32)) return false;
+    return c3s2_lds_bytes(g) <= 160 * 1024 && (size_t)g.N * g.P * g.Q * HK * 2 < 0x7fffffffu &&
+           (size_t)g.N * g.H * g.W * 3 * 2 < 0x7fffffffu;
 }
 
-int c3s2_grid(const ConvGeom &g) { return g.N * c3_bands(g); }
+int c3s2_grid(const ConvGeom &g)
+{
+    const long steps = (long)g.N * ((g.P * g.Q + SP - 1) / SP);
+    return (int)std::min<long>(steps, 256);
+}
 
 size_t c3s2_lds_bytes(const ConvGeom &g)
 {
-    const int NR = 2 * (TP - 1) + g.R;
-    const size_t stage = (size_t)KOUT * (g.R * 64 + 16) + (size_t)NR * c3_lw(g) * 8;
-    const size_t zstage = (size_t)32 * NBLK * KOUT * 2;   // every pixel block of a band
-    return std::max({stage, zstage, (size_t)32 * NT * 4});
+    return std::max((size_t)c3p_nslot(g) * c3p_lw(g) * 8 + 2 * STG_BYTES, (size_t)STATS_BYTES);
 }
 
-size_t c3s2_wexp_bytes(const ConvGeom &g) { return (size_t)KOUT * g.R * 32 * 2; }
+size_t c3s2_wexp_bytes(const ConvGeom &g) { return (size_t)HK * g.R * 32 * 2; }
 
 hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *wexp,
                                   uint16_t *z, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    hipError_t e = launch(widen_filter_c3_kernel, dim3((KOUT * g.R * 32 + NT - 1) / NT), dim3(NT), 0, st, e0, nullptr,
-                          w, g.R, g.S, wexp);
+    hipError_t e = launch(widen_filter_c3_kernel, dim3((HK * g.R * 32 + 255) / 256), dim3(256), 0, st, e0, nullptr, w,
+                          g.R, g.S, wexp);
     if (e != hipSuccess) return e;
-    C3Params prm;
+    C3PParams prm;
     prm.x = x;
     prm.wexp = wexp;
     prm.z = z;
@@ -310,19 +342,19 @@ hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const ui
     prm.pw = g.pw;
     prm.P = g.P;
     prm.Q = g.Q;
-    prm.bands = c3_bands(g);
-    prm.LW = c3_lw(g);
-    prm.RB = prm.LW * 8;
-    prm.WRB = g.R * 64 + 16;
+    prm.slot_bytes = c3p_lw(g) * 8;
+    prm.nslot = c3p_nslot(g);
+    prm.mQ = (uint32_t)(((1ull << 32) + g.Q - 1) / g.Q);                 // 0 for Q = 1
+    prm.mG = (uint32_t)(((1ull << 32) + g.W / 8 - 1) / (g.W / 8));       // 0 for W = 8
     const size_t lds = c3s2_lds_bytes(g);
     static bool attr_set = false;
     if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)conv_c3s2_stats_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                80 * 1024);
+        e = hipFuncSetAttribute((const void *)conv_c3s2_persist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    return launch(conv_c3s2_stats_kernel, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
+    return launch(conv_c3s2_persist_kernel, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
 }
 
 }  // namespace cbr

@@ -96,14 +96,19 @@ def test_train_forward_persistent_3x3(g):
     H.check_train(g, d, res, ora)
 
 
-# The first-layer kernel (3 input channels, stride 2, 64 output channels, W % 8 == 0,
-# odd padding): several bands, a partial last band, short and narrow images, 3x3 and
-# 5x5 filters.
+# The first-layer kernel (3 input channels, stride 2, 64 output channels, W % 8 == 0;
+# persistent over ranges of 256-pixel steps): partial last steps, short and narrow images,
+# 3x3, 5x5 and non-square filters, ranges starting inside an image and crossing image
+# ends, one 8-pixel piece per input row.
 FIRST_LAYER_GEOMS = [
     Geometry(2, 32, 32, 3, 64, 7, 7, 2, 3),
     Geometry(1, 24, 40, 3, 64, 7, 7, 2, 3),
     Geometry(3, 17, 16, 3, 64, 3, 3, 2, 1),      # 9 output rows: partial last band
     Geometry(2, 40, 8, 3, 64, 5, 5, 2, 1),       # 3 output columns
+    Geometry(1, 224, 224, 3, 64, 7, 7, 2, 3),    # one image: 49 single-step ranges, most mid-image
+    Geometry(300, 16, 16, 3, 64, 3, 3, 2, 1),    # 300 one-step images over 256 workgroups
+    Geometry(3, 9, 8, 3, 64, 3, 6, 2, 1, pad_w=0),   # two output columns, one 8-pixel piece per row
+    Geometry(2, 31, 24, 3, 64, 4, 6, 2, 2),      # even padding, R != S
 ]
 
 
