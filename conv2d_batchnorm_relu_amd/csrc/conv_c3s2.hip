@@ -31,7 +31,7 @@ namespace {
 
 using namespace persist;
 
-constexpr int KMAX = 14;   // k-steps: two per filter row, R <= 7
+constexpr int MAXR = 7;    // filter rows
 
 struct C3PParams {
     const uint16_t *x;      // N x H x W x 3
@@ -70,11 +70,40 @@ __global__ __launch_bounds__(256) void widen_filter_c3_kernel(const uint16_t *__
     }
 }
 
+// A block's fragment reads are inline assembly issued together, and each MFMA waits
+// (explicit lgkmcnt, tied to its fragment) for exactly its own read: left to itself the
+// compiler placed every read right before its MFMA behind a full wait, one LDS latency
+// per MFMA.  LDS operations complete in order, so "at most n outstanding" means all but
+// the n newest are done (scalar memory operations only add to the count).
+__device__ __forceinline__ bf16x8 lds_rd(uint32_t addr)
+{
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8 &x)
+{
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int R, int T>
+__device__ __forceinline__ void mfma_chain(f32x16 &acc, const bf16x8 (&wf)[2 * R], bf16x8 (&xf)[2 * R])
+{
+    lds_wait<2 * R - 1 - T>(xf[T]);
+    __builtin_amdgcn_sched_barrier(0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[T], xf[T], acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (T + 1 < 2 * R) mfma_chain<R, T + 1>(acc, wf, xf);
+}
+
 // Eight pixels of an input row: 48 bytes of x (three 16-byte loads).
 struct Piece {
     u32x4 a, b, d;
 };
 
+// R (the filter's rows) is a template parameter: the k-loops are then straight-line code
+// (2R fragment reads, then 2R MFMAs), with no run-time guards between the reads.
+template <int R>
 __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -82,7 +111,7 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int simd = wave & (NSIMD - 1), j = wave >> 2;
     const int hi = lane >> 5, l32 = lane & 31;
-    const int H = p.H, W = p.W, Q = p.Q, R = p.R, SB = p.slot_bytes, NSLOT = p.nslot;
+    const int H = p.H, W = p.W, Q = p.Q, SB = p.slot_bytes, NSLOT = p.nslot;
     const int PQ = p.P * Q;
     const int spi = (PQ + SP - 1) / SP;                       // steps per image
     // This workgroup's steps: a contiguous range [t0, t1) of the N * spi steps of the batch
@@ -90,16 +119,15 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
     const long tot = (long)p.N * spi;
     const int t0 = (int)(tot * blockIdx.x / gridDim.x), t1 = (int)(tot * (blockIdx.x + 1) / gridDim.x);
     const int gpr = W / 8;                                    // 8-pixel pieces per input row
-    const int nks = 2 * R;
+    constexpr int nks = 2 * R;
     uint8_t *const stg0 = lds + NSLOT * SB;                   // two z staging buffers
 
     // Filter fragment t (k-step t): lane (l32, hi) holds output channel 32j + l32, tap row
     // t / 2, taps 4 (t % 2) + 2 hi and + 1, four channels each: 16 bytes of wexp.
-    bf16x8 wf[KMAX];
+    bf16x8 wf[nks];
 #pragma unroll
-    for (int t = 0; t < KMAX; ++t)
-        wf[t] = t < nks ? *(const bf16x8 *)(p.wexp + ((size_t)(32 * j + l32) * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi)
-                        : bf16x8{};
+    for (int t = 0; t < nks; ++t)
+        wf[t] = *(const bf16x8 *)(p.wexp + ((size_t)(32 * j + l32) * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi);
 
     // Piece g of input row h of image n (zeros outside the image), and its widened store
     // into the row's slot: pixel u of the row at byte (pw + u) * 8 of the slot.
@@ -234,21 +262,18 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
             int sl0 = fslot + 2 * (pr - ofr);
             while (sl0 >= NSLOT) sl0 -= NSLOT;
             const int colb = 16 * q + 16 * hi;
-            bf16x8 xf[KMAX];
+            const uint32_t lbase = (uint32_t)(uintptr_t)(lds_u8 *)lds + colb;
+            bf16x8 xf[nks];
 #pragma unroll
-            for (int tt = 0; tt < KMAX; ++tt) {
-                if (tt < nks) {
-                    int sl = sl0 + (tt >> 1);
-                    if (sl >= NSLOT) sl -= NSLOT;
-                    xf[tt] = *(const bf16x8 *)(lds + sl * SB + colb + 32 * (tt & 1));
-                }
+            for (int tt = 0; tt < nks; ++tt) {
+                int sl = sl0 + (tt >> 1);
+                if (sl >= NSLOT) sl -= NSLOT;
+                xf[tt] = lds_rd(lbase + sl * SB + 32 * (tt & 1));
             }
             f32x16 acc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < KMAX; ++tt)
-                if (tt < nks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[tt], xf[tt], acc, 0, 0, 0);
+            mfma_chain<R, 0>(acc, wf, xf);
             if (full)
                 epilogue<false>(acc, use, true, first, stg, px, j, hi, c, s1, s2, cnt);
             else
@@ -293,11 +318,24 @@ int c3p_lw(const ConvGeom &g)
 // + R, where the output rows of 2 SP consecutive pixels span at most (2 SP - 1) / Q + 2.
 int c3p_nslot(const ConvGeom &g) { return 2 * ((2 * SP - 1) / g.Q + 1) + g.R; }
 
+template <int R>
+hipError_t launch_c3p(const C3PParams &prm, const ConvGeom &g, size_t lds, hipStream_t st, hipEvent_t e1)
+{
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)conv_c3s2_persist_kernel<R>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    return launch(conv_c3s2_persist_kernel<R>, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
+}
+
 }  // namespace
 
 bool c3s2_eligible(const ConvGeom &g)
 {
-    if (!(g.C == 3 && g.K == HK && g.sh == 2 && g.sw == 2 && g.R >= 1 && g.R <= 7 && g.S >= 1 && g.S <= 8 &&
+    if (!(g.C == 3 && g.K == HK && g.sh == 2 && g.sw == 2 && g.R >= 1 && g.R <= MAXR && g.S >= 1 && g.S <= 8 &&
           g.W % 8 == 0 && g.ph >= 0 && g.pw >= 0 && g.P >= 1 && g.Q >= 1))
         return false;
     // zero columns left and right of the image: at most 16 per row
@@ -347,14 +385,16 @@ hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const ui
     prm.mQ = (uint32_t)(((1ull << 32) + g.Q - 1) / g.Q);                 // 0 for Q = 1
     prm.mG = (uint32_t)(((1ull << 32) + g.W / 8 - 1) / (g.W / 8));       // 0 for W = 8
     const size_t lds = c3s2_lds_bytes(g);
-    static bool attr_set = false;
-    if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)conv_c3s2_persist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
+    switch (g.R) {
+    case 1: return launch_c3p<1>(prm, g, lds, st, e1);
+    case 2: return launch_c3p<2>(prm, g, lds, st, e1);
+    case 3: return launch_c3p<3>(prm, g, lds, st, e1);
+    case 4: return launch_c3p<4>(prm, g, lds, st, e1);
+    case 5: return launch_c3p<5>(prm, g, lds, st, e1);
+    case 6: return launch_c3p<6>(prm, g, lds, st, e1);
+    case 7: return launch_c3p<7>(prm, g, lds, st, e1);
+    default: return hipErrorInvalidValue;   // not eligible
     }
-    return launch(conv_c3s2_persist_kernel, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
 }
 
 }  // namespace cbr
