@@ -230,21 +230,27 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
             }
         }
         // The previous step's z: channel half 0's waves store the first half of its runs,
-        // the others the second half.
-        if (prev.nq > 0) {
-            const uint8_t *sb = stg0 + pbuf * STG_BYTES;
+        // the others the second half.  Half 0 stores at the step's start and half 1 after
+        // its first block, so the two waves of a SIMD leave the barrier out of phase: one's
+        // k-loop runs beside the other's stores or epilogue instead of both competing for
+        // the MFMA unit and then both leaving it idle.
+        auto store_prev = [&]() {
+            if (prev.nq > 0) {
+                const uint8_t *sb = stg0 + pbuf * STG_BYTES;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int q = simd + NSIMD * (4 * j + k);
-                const int px = 8 * q + (lane >> 3);
-                prev.d[k] = *(const u32x4 *)(sb + px * PXB + (((lane & 7) ^ perm(px)) << 4));
-            }
+                for (int k = 0; k < 4; ++k) {
+                    const int q = simd + NSIMD * (4 * j + k);
+                    const int px = 8 * q + (lane >> 3);
+                    prev.d[k] = *(const u32x4 *)(sb + px * PXB + (((lane & 7) ^ perm(px)) << 4));
+                }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int q = simd + NSIMD * (4 * j + k);
-                __builtin_amdgcn_raw_buffer_store_b128(prev.d[k], prev.zr, q * 1024 + lane * 16, 0, Z_POLICY);
+                for (int k = 0; k < 4; ++k) {
+                    const int q = simd + NSIMD * (4 * j + k);
+                    __builtin_amdgcn_raw_buffer_store_b128(prev.d[k], prev.zr, q * 1024 + lane * 16, 0, Z_POLICY);
+                }
             }
-        }
+        };
+        if (j == 0 || nb == 0) store_prev();
         const int cbuf = pbuf ^ 1;
         uint8_t *const stg = stg0 + cbuf * STG_BYTES;
         // slot of input row 2 ofr - ph (tap row 0 of the step's first output row)
@@ -279,6 +285,7 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_persist_kernel(C3PParams p)
             else
                 epilogue<true>(acc, use, (px ^ 16) < npix, first, stg, px, j, hi, c, s1, s2, cnt);
             first = false;
+            if (bb == 0 && j == 1) store_prev();
         }
         // The next step's rows into their slots (no wave of this step reads them).
         if (nx_on) store_piece(nx_h, nx_g, nx);
