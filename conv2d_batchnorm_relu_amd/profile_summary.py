@@ -171,13 +171,40 @@ def write_md(res, path, command):
         f.write("\n".join(lines))
 
 
+def write_trace_md(stats_csv, path, command, note=""):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv: calls and
+    average / min / max duration per kernel, longest total first."""
+    rows = []
+    with open(stats_csv, newline="") as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda r: -r[2])
+    lines = ["# Kernel durations, all bench workloads (rocprofv3 --kernel-trace --stats)", "",
+             "Command (`<repo>` is the repository root, `<out>` the output directory):", "", "```",
+             command.strip(), "```", "", f"Library sources sha256: `{sources_sha256()}`.", ""]
+    if note:
+        lines += [note.strip(), ""]
+    lines += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for name, calls, _, avg, mn, mx in rows:
+        lines.append(f"| `{name[:90]}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--root", required=True)
+    ap.add_argument("--root", help="counter passes: <root>/<workload>/<pass>/*counter_collection.csv")
     ap.add_argument("--md", required=True)
-    ap.add_argument("--json", required=True)
+    ap.add_argument("--json")
+    ap.add_argument("--trace-stats", help="instead: summarise this kernel_stats.csv of a kernel-trace run")
+    ap.add_argument("--note", default="", help="a paragraph added under the command (trace summaries)")
     ap.add_argument("--command", default="", help="the profiling command line(s), quoted in the summary")
     args = ap.parse_args(argv)
+    if args.trace_stats:
+        write_trace_md(args.trace_stats, args.md, args.command, args.note)
+        print(f"wrote {args.md}")
+        return
     res = summarize(args.root)
     with open(args.json, "w") as f:
         json.dump(res, f, indent=1)
