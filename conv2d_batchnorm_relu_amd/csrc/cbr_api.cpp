@@ -5,7 +5,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/cbr.h"
 #include "cbr_launch.h"
@@ -43,7 +45,23 @@ int make_geom(const cbr_shape *s, ConvGeom *g)
     return CBR_OK;
 }
 
+std::mutex g_lds_mu;
+std::map<std::pair<const void *, int>, int> g_lds_limit;   // (function, device) -> bytes set
+
 }  // namespace
+
+hipError_t cbr::raise_lds_limit(const void *func, int bytes)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    int &have = g_lds_limit[std::make_pair(func, dev)];
+    if (have >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
 
 // The data gradient as a stride-1 forward convolution of dz with the flipped filter.
 ConvGeom cbr::dgrad_geom(const ConvGeom &g)
@@ -136,8 +154,8 @@ SideStream *side_stream()
         if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
             hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
-            if (a) hipEventDestroy(a);
-            hipStreamDestroy(st);
+            if (a) (void)hipEventDestroy(a);
+            (void)hipStreamDestroy(st);
             return nullptr;
         }
         ss.fork = a;

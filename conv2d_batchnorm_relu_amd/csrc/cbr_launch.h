@@ -43,6 +43,11 @@ inline hipError_t launch(Kern k, dim3 grid, dim3 block, uint32_t shmem, hipStrea
     return hipGetLastError();
 }
 
+// Raises func's dynamic-LDS limit to at least `bytes` on the current device, calling
+// hipFuncSetAttribute only the first time a (function, device) pair needs more (the
+// attribute is per device).  Thread-safe.
+hipError_t raise_lds_limit(const void *func, int bytes);
+
 // Kernel plans.  Each convolution stage of a call -- the training forward's conv, the
 // inference / conv + bias conv, the data gradient's conv and the weight gradient -- runs
 // one of these kernels and tile shapes.  resolve_plan picks it per geometry: a tuning

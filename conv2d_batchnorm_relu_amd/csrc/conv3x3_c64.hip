@@ -501,13 +501,8 @@ hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const 
     const uint32_t mW = (uint32_t)(((1ull << 32) + g.W - 1) / g.W);
     HaloParams prm{x, w, z, partials, g.N, g.H, g.W, (g.W + 2) * PXB, halo_nslot(g), mW};
     const size_t lds = halo_lds_bytes(g);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)conv3x3_c64_stats_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)HALO_MAX_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = raise_lds_limit((const void *)conv3x3_c64_stats_kernel, (int)lds);
+    if (e != hipSuccess) return e;
     const dim3 grid(halo_grid(g)), block(NT);
     if (e0 || e1)
         hipExtLaunchKernelGGL(conv3x3_c64_stats_kernel, grid, block, (uint32_t)lds, st, e0, e1, 0, prm);

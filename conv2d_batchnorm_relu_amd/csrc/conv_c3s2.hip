@@ -328,13 +328,8 @@ int c3p_nslot(const ConvGeom &g) { return 2 * ((2 * SP - 1) / g.Q + 1) + g.R; }
 template <int R>
 hipError_t launch_c3p(const C3PParams &prm, const ConvGeom &g, size_t lds, hipStream_t st, hipEvent_t e1)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)conv_c3s2_persist_kernel<R>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = raise_lds_limit((const void *)conv_c3s2_persist_kernel<R>, (int)lds);
+    if (e != hipSuccess) return e;
     return launch(conv_c3s2_persist_kernel<R>, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
 }
 

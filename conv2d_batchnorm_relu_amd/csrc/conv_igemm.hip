@@ -534,9 +534,7 @@ size_t ig_lds_bytes(const ConvGeom &g, int epi, int plan)
 template <int MI, int NJ, int WGM, int WGN, int BK, int NSTAGE, int EPI>
 hipError_t ig_launch_one(const IgParams &prm, int grid, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const hipError_t e =
-        hipFuncSetAttribute((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = raise_lds_limit((const void *)conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI>, (int)lds);
     if (e != hipSuccess) return e;
     return launch(conv_igemm_kernel<MI, NJ, WGM, WGN, BK, NSTAGE, EPI>, dim3(grid), dim3(64 * WGM * WGN),
                   (uint32_t)lds, st, e0, e1, prm);

@@ -701,8 +701,7 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, co
         tp.rows_per_split = p.rows_per_split;
         tp.dpq = fast_div((uint32_t)(g.P * g.Q));
         tp.dq = fast_div((uint32_t)g.Q);
-        hipError_t e = hipFuncSetAttribute((const void *)conv_wgrad_tr_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)TR_LDS);
+        hipError_t e = raise_lds_limit((const void *)conv_wgrad_tr_kernel, (int)TR_LDS);
         if (e != hipSuccess) return e;
         const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;
         e = launch(conv_wgrad_tr_kernel, dim3(p.tiles_n, p.tiles_m, p.splits), dim3(TR_NT), (uint32_t)TR_LDS, st, e0,
