@@ -12,7 +12,9 @@
 //     four consecutive channels of one pixel).  Large wave tiles keep the LDS fragment
 //     reads per MFMA low.
 //   * Reduction slices of BK = 64 (C % 64 == 0) or 32 elements, inside one filter tap,
-//     move from global memory straight into LDS (buffer-to-LDS loads, 128- or 64-byte
+//     taken channel slice by channel slice, all taps of one before the next (the rows the
+//     taps re-read are then BK channels wide instead of C, a smaller set for the XCD's L2
+//     to hold), move from global memory straight into LDS (buffer-to-LDS loads, 128- or 64-byte
 //     rows, 16-byte chunks XOR-permuted by row so fragment reads are conflict-free),
 //     NSTAGE slices in flight.
 //     Padding taps and pixels past the range get out-of-range buffer offsets (zeros).  The slice
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
         }
         const uint32_t dst = (uint32_t)((g % NSTAGE) * STAGE_B);
         const int toff = 2 * ((dr * p.W + ds) * p.C + dc0);
-        const int koff = 2 * BK * dks;
+        const int koff = 2 * ((dr * p.S + ds) * p.C + dc0);
         const int tapbits = (1 << dr) | (1 << (16 + ds));
 #pragma unroll
         for (int t = 0; t < IPW; ++t) {
@@ -246,14 +248,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_igemm_kernel(IgParams 
                 buffer_load_lds16(wr, (lds_u8 *)lds + dst + u * 1024, d_off[t] + koff);
             }
         }
-        // next slice's tap and channel offset
+        // next slice: the next tap of this channel slice, then the next channel slice
         if (++dks == p.ksteps) dks = 0;
-        dc0 += BK;
-        if (dc0 == p.C) {
-            dc0 = 0;
-            if (++ds == p.S) {
-                ds = 0;
-                ++dr;
+        if (++ds == p.S) {
+            ds = 0;
+            if (++dr == p.R) {
+                dr = 0;
+                dc0 += BK;
             }
         }
     };
