@@ -103,7 +103,7 @@ def test_train_forward_persistent_3x3(g):
 FIRST_LAYER_GEOMS = [
     Geometry(2, 32, 32, 3, 64, 7, 7, 2, 3),
     Geometry(1, 24, 40, 3, 64, 7, 7, 2, 3),
-    Geometry(3, 17, 16, 3, 64, 3, 3, 2, 1),      # 9 output rows: partial last band
+    Geometry(3, 17, 16, 3, 64, 3, 3, 2, 1),      # 9 x 8 outputs: one partial step per image
     Geometry(2, 40, 8, 3, 64, 5, 5, 2, 1),       # 3 output columns
     Geometry(1, 224, 224, 3, 64, 7, 7, 2, 3),    # one image: 49 single-step ranges, most mid-image
     Geometry(300, 16, 16, 3, 64, 3, 3, 2, 1),    # 300 one-step images over 256 workgroups
