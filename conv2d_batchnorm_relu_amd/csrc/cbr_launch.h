@@ -69,7 +69,8 @@ enum Plan {
     PLAN_BWD_SERIAL = 9,    // backward: weight gradient, then data gradient, one stream
     PLAN_BWD_OVERLAP = 10,  // backward: weight gradient on a second stream beside the data gradient
     PLAN_BWD_FUSED = 11,    // backward: no dz tensor; both gradients form dz while staging (K <= 256, C % 8 == 0)
-    NPLANS = 12
+    PLAN_WG_TR_WIDE = 12,   // weight gradient with transposed LDS reads, 256 x 256 tiles (C % 256, K % 256)
+    NPLANS = 13
 };
 // g is always the layer's geometry (cbr_shape); for STAGE_DGRAD the plan runs, and is
 // checked on, the data gradient's convolution dgrad_geom(g).
@@ -120,12 +121,13 @@ int bnbwd_blocks(int M, int K);
 
 // Split factor of the weight-gradient reduction over output pixels.
 struct WgradPlan {
-    bool tr;          // transposed-read kernel (C % 128 == 0, K % 256 == 0)
+    bool tr;          // transposed-read kernel (C % bn == 0, K % 256 == 0)
     int bm, bn;       // tile over (K output channels) x (R*S*C)
     int tiles_m, tiles_n, splits;
     int rows_per_split;   // output pixels per split (multiple of the pixel step)
 };
 bool wgrad_tr_eligible(const ConvGeom &g);
+bool wgrad_tr_wide_eligible(const ConvGeom &g);
 WgradPlan wgrad_plan(const ConvGeom &g, int plan);
 
 // Persistent large-tile implicit-GEMM conv (C % 32 == 0, K a multiple of the chunk's

@@ -42,6 +42,7 @@ bool plan_eligible(const ConvGeom &layer, int stage, int plan)
     case PLAN_GEN_128X64: return is_conv_stage(stage);
     case PLAN_WG_TR: return stage == STAGE_WGRAD && wgrad_tr_eligible(g);
     case PLAN_WG_GEN: return stage == STAGE_WGRAD;
+    case PLAN_WG_TR_WIDE: return stage == STAGE_WGRAD && wgrad_tr_wide_eligible(g);
     case PLAN_BWD_SERIAL: return stage == STAGE_BWD;
     case PLAN_BWD_OVERLAP: return stage == STAGE_BWD && layer.sh == 1 && layer.sw == 1;
     case PLAN_BWD_FUSED: return stage == STAGE_BWD && layer.K <= 256 && layer.C % 8 == 0;
@@ -96,6 +97,7 @@ const char *plan_name(int plan)
     case PLAN_GEN_128X64: return "generic_128x64";
     case PLAN_WG_TR: return "wgrad_transposed_read";
     case PLAN_WG_GEN: return "wgrad_generic";
+    case PLAN_WG_TR_WIDE: return "wgrad_transposed_read_256x256";
     case PLAN_BWD_SERIAL: return "backward_serial";
     case PLAN_BWD_OVERLAP: return "backward_wgrad_beside_dgrad";
     case PLAN_BWD_FUSED: return "backward_dz_formed_in_gradients";

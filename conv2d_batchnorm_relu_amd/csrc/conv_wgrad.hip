@@ -415,19 +415,34 @@ __device__ __forceinline__ bf16x8 tr_join(i16x4 lo, i16x4 hi)
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-constexpr int TR_BM = 256, TR_BN = 128, TR_WGM = 4, TR_WGN = 2, TR_NSTAGE = 3;
-constexpr int TR_NW = TR_WGM * TR_WGN, TR_NT = 64 * TR_NW;
-constexpr int TR_BKM = 64;                         // pixels per slice
-constexpr int TR_RSA = 2 * TR_BM, TR_RSB = 2 * TR_BN;   // row bytes of the dz and x slices
-constexpr int TR_STAGE_A = TR_BKM * TR_RSA, TR_STAGE = TR_STAGE_A + TR_BKM * TR_RSB;
-constexpr int TR_NA = TR_STAGE_A / 1024, TR_NINS = TR_STAGE / 1024;   // 1 KB load instructions
-constexpr int TR_IPW = TR_NINS / TR_NW;
-constexpr size_t TR_LDS = (size_t)TR_NSTAGE * TR_STAGE;
-static_assert(TR_NINS % TR_NW == 0, "load instructions per wave");
+// Tile configurations: BM output channels x BN filter positions (one tap, BN input
+// channels) per workgroup, WGM x WGN waves, NSTAGE slices of 64 pixels in LDS.
+template <int BM_, int BN_, int WGM_, int WGN_, int NSTAGE_>
+struct TrCfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NSTAGE = NSTAGE_;
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int BKM = 64;                              // pixels per slice
+    static constexpr int RSA = 2 * BM, RSB = 2 * BN;            // row bytes of the dz and x slices
+    static constexpr int STAGE_A = BKM * RSA, STAGE = STAGE_A + BKM * RSB;
+    static constexpr int NA = STAGE_A / 1024, NINS = STAGE / 1024;   // 1 KB load instructions
+    static constexpr int IPW = NINS / NW;
+    static constexpr size_t LDS = (size_t)NSTAGE * STAGE;
+    static_assert(NINS % NW == 0 && NA % NW == 0, "load instructions per wave");
+    static_assert(NSTAGE == 2 || NSTAGE == 3, "slices in LDS");
+};
+// 256 x 128 tiles, eight 64 x 64 wave tiles, three slices in flight (PLAN_WG_TR), and
+// 256 x 256 tiles, eight 128 x 64 wave tiles (a quarter fewer fragment bytes per MFMA),
+// two slices (PLAN_WG_TR_WIDE).
+using TrStd = TrCfg<256, 128, 4, 2, 3>;
+using TrWide = TrCfg<256, 256, 2, 4, 2>;
 
-__global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p)
+template <typename C>
+__global__ __launch_bounds__(C::NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p)
 {
-    constexpr int MI = TR_BM / (32 * TR_WGM), NJ = TR_BN / (32 * TR_WGN);   // 2 x 2 blocks per wave
+    constexpr int TR_BM = C::BM, TR_BN = C::BN, TR_WGM = C::WGM, TR_WGN = C::WGN, TR_NSTAGE = C::NSTAGE;
+    constexpr int TR_NW = C::NW, TR_BKM = C::BKM, TR_RSA = C::RSA, TR_RSB = C::RSB;
+    constexpr int TR_STAGE_A = C::STAGE_A, TR_STAGE = C::STAGE, TR_NA = C::NA, TR_IPW = C::IPW;
+    constexpr int MI = TR_BM / (32 * TR_WGM), NJ = TR_BN / (32 * TR_WGN);   // blocks per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const uint32_t lbase = (uint32_t)(uintptr_t)(lds_u8 *)lds;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -588,9 +603,14 @@ __global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
         }
         tr_lgkm_wait<0>();
         tie_set(af[1], bf[1]);
-        // slice t + 1 landed (slice t + 2 may stay in flight); every wave is past slice t
-        if (t + 2 < nsteps) tr_vm_wait<TR_IPW>();
-        else if (t + 1 < nsteps) tr_vm_wait<0>();
+        // slice t + 1 landed (with three stages slice t + 2 may stay in flight); every wave
+        // is past slice t
+        if constexpr (TR_NSTAGE == 3) {
+            if (t + 2 < nsteps) tr_vm_wait<TR_IPW>();
+            else if (t + 1 < nsteps) tr_vm_wait<0>();
+        } else {
+            if (t + 1 < nsteps) tr_vm_wait<0>();
+        }
         tr_barrier();
         if (t + 1 < nsteps) read_frags(af[0], bf[0], t + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -615,28 +635,31 @@ __global__ __launch_bounds__(TR_NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
 
 }  // namespace
 
-bool wgrad_tr_eligible(const ConvGeom &g)
+bool wgrad_tr_eligible(const ConvGeom &g, int bn)
 {
     const double xbytes = 2.0 * g.N * g.H * g.W * g.C, zbytes = 2.0 * g.M * g.K;
-    return g.C % TR_BN == 0 && g.K % TR_BM == 0 && g.M > 0 && xbytes < 2147483648.0 && zbytes < 2147483648.0;
+    return g.C % bn == 0 && g.K % TrStd::BM == 0 && g.M > 0 && xbytes < 2147483648.0 && zbytes < 2147483648.0;
 }
+bool wgrad_tr_eligible(const ConvGeom &g) { return wgrad_tr_eligible(g, TrStd::BN); }
+bool wgrad_tr_wide_eligible(const ConvGeom &g) { return wgrad_tr_eligible(g, TrWide::BN); }
 
 WgradPlan wgrad_plan(const ConvGeom &g, int plan)
 {
     const int M = g.M, K = g.K, Kg = g.Kg;
     WgradPlan p;
-    p.tr = plan == PLAN_WG_TR;
+    p.tr = plan == PLAN_WG_TR || plan == PLAN_WG_TR_WIDE;
     if (p.tr) {
-        // one workgroup per CU: 256 x 128 tiles, the pixel range split to fill the rest
-        p.bm = TR_BM;
-        p.bn = TR_BN;
-        p.tiles_m = K / TR_BM;
-        p.tiles_n = Kg / TR_BN;
+        // one workgroup per CU: 256 x 128 (or 256 x 256) tiles, the pixel range split to
+        // fill the rest
+        p.bm = TrStd::BM;
+        p.bn = plan == PLAN_WG_TR_WIDE ? TrWide::BN : TrStd::BN;
+        p.tiles_m = K / p.bm;
+        p.tiles_n = Kg / p.bn;
         const int tiles = p.tiles_m * p.tiles_n;
-        const int steps = (M + TR_BKM - 1) / TR_BKM;
+        const int steps = (M + TrStd::BKM - 1) / TrStd::BKM;
         const int want = std::max(1, std::min(steps, 256 / tiles));
         const int steps_per = (steps + want - 1) / want;
-        p.rows_per_split = steps_per * TR_BKM;
+        p.rows_per_split = steps_per * TrStd::BKM;
         p.splits = (M + p.rows_per_split - 1) / p.rows_per_split;
         return p;
     }
@@ -701,11 +724,15 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, int plan, const uint16_t *dz, co
         tp.rows_per_split = p.rows_per_split;
         tp.dpq = fast_div((uint32_t)(g.P * g.Q));
         tp.dq = fast_div((uint32_t)g.Q);
-        hipError_t e = raise_lds_limit((const void *)conv_wgrad_tr_kernel, (int)TR_LDS);
-        if (e != hipSuccess) return e;
         const hipEvent_t ek = p.splits == 1 ? e1 : nullptr;
-        e = launch(conv_wgrad_tr_kernel, dim3(p.tiles_n, p.tiles_m, p.splits), dim3(TR_NT), (uint32_t)TR_LDS, st, e0,
-                   ek, tp);
+        auto run = [&](auto cfg) {
+            using C = decltype(cfg);
+            hipError_t e = raise_lds_limit((const void *)conv_wgrad_tr_kernel<C>, (int)C::LDS);
+            if (e != hipSuccess) return e;
+            return launch(conv_wgrad_tr_kernel<C>, dim3(p.tiles_n, p.tiles_m, p.splits), dim3(C::NT),
+                          (uint32_t)C::LDS, st, e0, ek, tp);
+        };
+        const hipError_t e = p.bn == TrWide::BN ? run(TrWide{}) : run(TrStd{});
         if (e != hipSuccess || p.splits == 1) return e;
         const long n = (long)g.K * g.Kg;
         const int blocks = (int)std::min<long>((n + NT - 1) / NT, 8192);

@@ -28,7 +28,7 @@ import sys
 import time
 
 STAGES = {0: "train_conv", 1: "infer_conv", 2: "dgrad", 3: "wgrad", 4: "backward"}
-PLANS = range(1, 12)
+PLANS = range(1, 13)
 
 
 def resnet50_layers():

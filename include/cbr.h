@@ -217,7 +217,8 @@ int cbr_conv2d_bias(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
  * else the call falls back to 9), 11 backward with no dz tensor: both gradients form dz
  * from dy, z and the mask while staging their operands ([CBR] section 5.1 keeps the
  * masked gradient on chip; K <= 256 and C % 8 == 0; used only when dz is NULL, else
- * the call falls back to 9).
+ * the call falls back to 9), 12 weight gradient with transposed reads on 256 x 256 tiles
+ * (C % 256 == 0 and K % 256 == 0).
  *
  * cbr_plan_of: the plan the stage will run for this layer shape (> 0), or minus a status.
  * cbr_plan_eligible: 1 if the plan can run the stage for this shape, 0 if not, or minus
