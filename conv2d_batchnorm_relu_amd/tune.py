@@ -28,7 +28,6 @@ import sys
 import time
 
 STAGES = {0: "train_conv", 1: "infer_conv", 2: "dgrad", 3: "wgrad", 4: "backward"}
-PLANS = range(1, 13)
 
 
 def resnet50_layers():
@@ -73,6 +72,11 @@ def main(argv=None):
 
     lib = cbr._load()
     lib.cbr_plan_name.restype = ctypes.c_char_p
+    plans = []   # every plan id the library names (ids run from 1 without gaps)
+    for p in range(1, 64):
+        if lib.cbr_plan_name(p).decode() == "unknown":
+            break
+        plans.append(p)
     dev = torch.device("cuda:0")
     os.makedirs(args.out_dir, exist_ok=True)
 
@@ -133,7 +137,7 @@ def main(argv=None):
                 continue
             if stage in (2, 4) and st != 1:
                 continue   # the data gradient needs stride 1
-            cands = [p for p in PLANS if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
+            cands = [p for p in plans if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
             default = lib.cbr_plan_of(ctypes.byref(sp), stage)
             times = {}
             # a stage's plan is judged by the whole call that contains it, timed over

@@ -37,9 +37,19 @@ def lib():
     return L
 
 
+def all_plans():
+    """Every plan id the library names (ids run from 1 without gaps)."""
+    out = []
+    for p in range(1, 64):
+        if lib().cbr_plan_name(p).decode() == "unknown":
+            break
+        out.append(p)
+    return out
+
+
 def eligible(g, stage):
     sp = H.cshape(g)
-    return [p for p in range(1, 12) if lib().cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
+    return [p for p in all_plans() if lib().cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
 
 
 class forced:
@@ -93,8 +103,13 @@ def test_infer_conv_plan(g, plan):
 # + a stride-2 layer (no data gradient) and a layer whose generic weight gradient splits
 # the pixels more finely (15 splits) than the transposed-read one (12): the fused schedule
 # runs the generic kernel, so the workspace must hold its partials.
+# Two more layers for the 256 x 256 transposed-read weight gradient (C % 256 == 0): two
+# output-channel tiles with a ragged last pixel split, and a 1x1 layer with two taps'
+# worth of channels per tile row.
 @pytest.mark.parametrize("g", PLAN_GEOMS[:4] + [Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1),
-                                                Geometry(30, 8, 16, 256, 256, 3, 3, 1, 1)], ids=str)
+                                                Geometry(30, 8, 16, 256, 256, 3, 3, 1, 1),
+                                                Geometry(7, 9, 11, 256, 512, 3, 3, 1, 1),
+                                                Geometry(3, 10, 10, 512, 256, 1, 1, 1, 0)], ids=str)
 def test_backward_plans(g, stage):
     want_dx = g.sh == 1 and g.sw == 1
     if stage == 2 and not want_dx:
