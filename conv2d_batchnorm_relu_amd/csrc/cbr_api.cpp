@@ -135,7 +135,7 @@ BwdLayout bwd_layout(const ConvGeom &g, int wplan)
 // use with the device current and kept for the life of the process; default priority.
 struct SideStream {
     hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, flip = nullptr;
     std::mutex mu;   // held from each event record to the wait that consumes it
 };
 constexpr int MAX_DEVICES = 64;
@@ -150,16 +150,19 @@ SideStream *side_stream()
     SideStream &ss = g_side[dev];
     if (!ss.stream) {
         hipStream_t st = nullptr;
-        hipEvent_t a = nullptr, b = nullptr;
+        hipEvent_t a = nullptr, b = nullptr, c = nullptr;
         if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c, hipEventDisableTiming) != hipSuccess) {
             if (a) (void)hipEventDestroy(a);
+            if (b) (void)hipEventDestroy(b);
             (void)hipStreamDestroy(st);
             return nullptr;
         }
         ss.fork = a;
         ss.join = b;
+        ss.flip = c;
         ss.stream = st;
     }
     return &ss;
@@ -426,9 +429,25 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
     // weight gradient reads, the in-place hazard of the CBR page's section 5.2);
     // otherwise both run on the caller's stream, weight gradient first.
     const size_t xbytes = (size_t)g.N * g.H * g.W * g.C * 2;
-    SideStream *ss = nullptr;
-    if (dx && bplan == PLAN_BWD_OVERLAP && !ranges_overlap(dx, xbytes, x, xbytes))
-        ss = side_stream();
+    // The device's side stream (default priority): the data gradient's filter flip, which
+    // reads only w, runs on it beside the BN backward; with the overlap plan the weight
+    // gradient follows it there, beside the data gradient.  Its lock is held from the
+    // first event record to the last wait of this call.
+    const bool overlap = dx && bplan == PLAN_BWD_OVERLAP && !ranges_overlap(dx, xbytes, x, xbytes);
+    SideStream *ss = dx ? side_stream() : nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
+    if (ss) {
+        side_lock = std::unique_lock<std::mutex>(ss->mu);
+        // the side stream first waits for the caller's earlier work (w may have just been
+        // written on it)
+        if (stream_after(ss->stream, s, ss->fork) != hipSuccess) return CBR_E_HIP;
+        if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, ss->stream, nullptr, nullptr) != hipSuccess)
+            return CBR_E_HIP;
+        if (hipEventRecord(ss->flip, ss->stream) != hipSuccess) return CBR_E_HIP;
+    } else if (dx && launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, nullptr, nullptr) != hipSuccess) {
+        return CBR_E_HIP;
+    }
     // masked BN backward (CBR page 5.1) -> WGrad, DGrad (5.2; DGrad skipped for the first
     // layer, 5.3).
     if (launch_bn_backward(g.M, g.K, dy, (const uint8_t *)relu_mask, z, gamma, saved_mean, saved_invstd,
@@ -436,28 +455,25 @@ int cbr_backward_ev(const cbr_shape *shape, const uint16_t *x, const uint16_t *w
                            (float *)ws_at(workspace, L.coef), dgamma, dbeta, dzp, s, ev(events, 0),
                            ev(events, 1)) != hipSuccess)
         return CBR_E_HIP;
-    std::unique_lock<std::mutex> side_lock;
-    if (ss) {
-        side_lock = std::unique_lock<std::mutex>(ss->mu);
-        if (stream_after(ss->stream, s, ss->fork) != hipSuccess) return CBR_E_HIP;
-    }
+    if (overlap && ss && stream_after(ss->stream, s, ss->fork) != hipSuccess) return CBR_E_HIP;
+    const bool wg_side = overlap && ss;
     if (launch_conv_wgrad(g, wplan, dzp, x, (float *)ws_at(workspace, L.wpart), L.wflip - L.wpart, dw,
-                          ss ? ss->stream : s, ev(events, 2), ev(events, 3)) != hipSuccess)
+                          wg_side ? ss->stream : s, ev(events, 2), ev(events, 3)) != hipSuccess)
         return CBR_E_HIP;
-    if (ss && hipEventRecord(ss->join, ss->stream) != hipSuccess) return CBR_E_HIP;
+    if (wg_side && hipEventRecord(ss->join, ss->stream) != hipSuccess) return CBR_E_HIP;
     if (dx) {
-        uint16_t *wt = (uint16_t *)ws_at(workspace, L.wflip);
-        if (launch_flip_weights(g.K, g.R, g.S, g.C, w, wt, s, ev(events, 4), nullptr) != hipSuccess) return CBR_E_HIP;
+        if (ss && hipStreamWaitEvent(s, ss->flip, 0) != hipSuccess) return CBR_E_HIP;
         const ConvGeom d = dgrad_geom(g);
-        if (launch_conv_fprop(d, EPI_PLAIN, resolve_plan(g, STAGE_DGRAD), dzp, wt, nullptr, dx, nullptr, s, nullptr,
-                              ev(events, 5)) != hipSuccess)
+        // the dgrad stage's events bracket the conv (the flip ran beside the BN backward)
+        if (launch_conv_fprop(d, EPI_PLAIN, resolve_plan(g, STAGE_DGRAD), dzp, wt, nullptr, dx, nullptr, s,
+                              ev(events, 4), ev(events, 5)) != hipSuccess)
             return CBR_E_HIP;
     } else if (events && (hipEventRecord(ev(events, 4), s) != hipSuccess ||
                           hipEventRecord(ev(events, 5), s) != hipSuccess)) {
         return CBR_E_HIP;
     }
     // the caller's stream continues only once the weight gradient has finished
-    if (ss && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return CBR_E_HIP;
+    if (wg_side && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return CBR_E_HIP;
     return CBR_OK;
 }
 
