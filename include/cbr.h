@@ -144,10 +144,12 @@ int cbr_forward_infer(const cbr_shape *shape,
  * form of [CBR] 5.3, which skips the data gradient.  dx may alias x: the weight
  * gradient finishes reading x before the data gradient writes dx ([CBR] 5.2).
  * A non-NULL dx needs stride 1 in both directions.
- * When dx does not overlap x the weight gradient may run on a second stream that the
- * library keeps per device (forked from and joined back to `stream` with events, see
- * CBR_STAGE_BWD); the call's work is still complete when `stream` reaches its end.
- * Calls on one device from several host threads serialise their enqueueing around it.
+ * With a dx, the data gradient's filter flip (it reads only w) runs on a second stream
+ * that the library keeps per device, beside the BN backward; when dx does not overlap x
+ * the weight gradient may run there too (see CBR_STAGE_BWD).  Both are forked from and
+ * joined back to `stream` with events: the call's work is still complete when `stream`
+ * reaches its end.  Calls on one device from several host threads serialise their
+ * enqueueing around that stream.
  */
 int cbr_backward(const cbr_shape *shape,
                  const uint16_t *x, const uint16_t *w, const uint16_t *z,
