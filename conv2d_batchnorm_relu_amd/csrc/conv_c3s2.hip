@@ -176,8 +176,7 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         }
         return r;
     };
-    auto store_piece = [&](int sl, int g, const Piece &r) {
-        uint8_t *dst = lds + sl * SB + (p.pw + 8 * g) * 8;
+    auto store_piece_at = [&](uint8_t *dst, const Piece &r) {
         const uint32_t v[12] = {r.a[0], r.a[1], r.a[2], r.a[3], r.b[0], r.b[1], r.b[2], r.b[3], r.d[0], r.d[1], r.d[2], r.d[3]};
         // bf16 value t of the piece is half t % 2 of word t / 2; pixel e is values 3e .. 3e + 2
         auto half = [&](int t) { return (v[t >> 1] >> (16 * (t & 1))) & 0xffffu; };
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         for (int i = tid; i < nrows * gpr; i += WNT) {
             const int ri = div_m(i, p.mG);
             const int g = i - ri * gpr;
-            store_piece((2 * ofr + ri) % NSLOT, g, load_piece(n, 2 * ofr - p.ph + ri, g));
+            store_piece_at(lds + ((2 * ofr + ri) % NSLOT) * SB + (p.pw + 8 * g) * 8, load_piece(n, 2 * ofr - p.ph + ri, g));
         }
     }
 
@@ -355,9 +354,22 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     // that step reads), so each load has a whole step to land.
     struct Pieces {
         Piece d[PPT];
-        int sl[PPT], g[PPT];
+        int la[PPT];   // LDS byte offset of the widened piece
         bool on[PPT];
     };
+    // Piece k of this thread is, in every step, piece g of the ri-th row the step adds
+    // (i = et + 256 k = ri * W / 8 + g): its offsets from the step's first row, in x and in
+    // the ring, are fixed.
+    int p_ri[PPT], p_xo[PPT], p_lo[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int i = et + NET * k;
+        const int ri = div_m(i, p.mG);
+        const int g = i - ri * gpr;
+        p_ri[k] = ri;
+        p_xo[k] = ri * (W * 6) + g * 48;
+        p_lo[k] = ri * SB + (p.pw + 8 * g) * 8;
+    }
     // The rows step u adds after the range's previous step, at most PPT pieces per thread:
     // in the same image (u.s > 0), input rows 2 olr(u.s - 1) - ph + R .. 2 olr(u.s) - ph +
     // R - 1; an image's first step, its rows -ph .. 2 olr(0) - ph + R - 1.
@@ -389,17 +401,13 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         }
         if (!exists) nrows = 0;
         const int sl_0 = v0 % NSLOT;
+        const int xrow0 = (u.n * H + h0) * (W * 6);   // byte offset of the step's first row
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-            const int i = et + NET * k;
-            pc.on[k] = i < nrows * gpr;
-            const int ri = div_m(i, p.mG);
-            pc.g[k] = i - ri * gpr;
-            int sl = sl_0 + ri;
-            if (sl >= NSLOT) sl -= NSLOT;
-            pc.sl[k] = sl;
-            const int h = h0 + ri;
-            const int off = pc.on[k] && h >= 0 && h < H ? (((u.n * H + h) * W + 8 * pc.g[k]) * 3) * 2 : (int)0x80000000u;
+            const int ri = p_ri[k], h = h0 + ri;
+            pc.on[k] = ri < nrows;
+            pc.la[k] = sl_0 * SB + p_lo[k] - (sl_0 + ri >= NSLOT ? NSLOT * SB : 0);
+            const int off = pc.on[k] && h >= 0 && h < H ? xrow0 + p_xo[k] : (int)0x80000000u;
             pc.d[k].a = buf_ld(off);
             pc.d[k].b = buf_ld(off + 16);
             pc.d[k].d = buf_ld(off + 32);
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         // The next step's rows into their slots (no wave of this step reads them).
 #pragma unroll
         for (int k = 0; k < PPT; ++k)
-            if (cur.on[k]) store_piece(cur.sl[k], cur.g[k], cur.d[k]);
+            if (cur.on[k]) store_piece_at(lds + cur.la[k], cur.d[k]);
         // The barrier publishes this step's results and the next step's rows, and frees
         // the result buffer read here for the next step's MFMAs.
         lds_barrier();
