@@ -204,6 +204,17 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     assert fn(None, *([FAKE] * 6), 1e-5, 0.1, *([FAKE] * 8), 0) == 1
 
 
+def test_first_layer_geometries_take_the_first_layer_kernel(lib):
+    """Every geometry of the first-layer parity tests resolves to the first-layer kernel,
+    so those tests exercise it (and not a generic fallback)."""
+    from test_gpu_parity import FIRST_LAYER_GEOMS
+    L = cbr._load()
+    L.cbr_plan_name.restype = ctypes.c_char_p
+    for g in FIRST_LAYER_GEOMS:
+        sp = cbr.make_shape(g.n, g.h, g.w, g.c, g.k, g.r, g.s, g.stride, g.pad, stride_w=g.stride_w, pad_w=g.pad_w)
+        assert L.cbr_plan_name(L.cbr_plan_of(ctypes.byref(sp), 0)).decode() == "first_layer_c3s2", g
+
+
 def test_plan_interface(lib):
     """Kernel plans: the defaults of the benchmark layers, eligibility, the override and its
     validation, and the compiled-in table's entries (each eligible for its shape)."""

@@ -109,6 +109,11 @@ FIRST_LAYER_GEOMS = [
     Geometry(300, 16, 16, 3, 64, 3, 3, 2, 1),    # 300 one-step images over 256 workgroups
     Geometry(3, 9, 8, 3, 64, 3, 6, 2, 1, pad_w=0),   # two output columns, one 8-pixel piece per row
     Geometry(2, 31, 24, 3, 64, 4, 6, 2, 2),      # even padding, R != S
+    Geometry(4, 64, 64, 3, 64, 1, 1, 2, 0),      # a 1 x 1 filter: one k-step per chain
+    Geometry(2, 50, 40, 3, 64, 2, 2, 2, 0),      # R = 2, no padding
+    Geometry(5, 30, 24, 3, 64, 6, 4, 2, 2, pad_w=1),   # R = 6, padding (2, 1)
+    Geometry(3, 12, 8, 3, 64, 6, 6, 2, 2),       # one 24-pixel step per image, R = 6
+    Geometry(1, 300, 296, 3, 64, 7, 7, 2, 3),    # 150 output columns, 302-pixel ring rows
 ]
 
 
