@@ -104,7 +104,6 @@ struct Piece {
 };
 
 constexpr int WSP = 128;                 // output pixels per step: 4 blocks of 32, one per SIMD
-constexpr int WNT = NT;                  // threads: 8 waves, two per SIMD
 constexpr int NMW = NSIMD;               // MFMA waves 0..3, wave w on SIMD w
 constexpr int NEW = NSIMD;               // epilogue waves 4..7, wave w on SIMD w % 4
 constexpr int NET = NEW * 64;            // epilogue threads
@@ -140,7 +139,7 @@ __device__ __forceinline__ void mfma_chain_in(f32x16 &acc, const bf16x8 (&wf)[2 
 // runs beside the MFMAs of the other on each SIMD, where with every wave doing both the
 // two phases alternated.
 template <int R>
-__global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
+__global__ __launch_bounds__(NT, 1) void conv_c3s2_ws_kernel(C3PParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -163,7 +162,8 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     // and lives in slot v % nslot.  Consecutive images' rows follow each other, so the
     // first rows of the next image load during the last step of the previous one.
     // Piece g of input row h of image n (zeros outside the image), and its widened store
-    // into slot sl: pixel u of the row at byte (pw + u) * 8 of the slot.
+    // at dst (pixel u of a row at byte (pw + u) * 8 of its slot, so dst = slot base +
+    // (pw + 8 g) * 8).
     auto load_piece = [&](int n, int h, int g) {
         Piece r;
         if (h >= 0 && h < H) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     // widened pixel a read can reach).
     {
         const int lw = SB / 8, nz = lw - W;
-        for (int i = tid; i < NSLOT * nz; i += WNT) {
+        for (int i = tid; i < NSLOT * nz; i += NT) {
             const int sl = i / nz, c = i - sl * nz;
             const int col = c < p.pw ? c : W + c;
             *(u32x2 *)(lds + sl * SB + col * 8) = u32x2{0u, 0u};
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(WNT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         const int a = s * WSP, npix = min(WSP, PQ - a);
         const int ofr = div_m(a, p.mQ), olr = div_m(a + npix - 1, p.mQ);
         const int nrows = 2 * (olr - ofr) + R;
-        for (int i = tid; i < nrows * gpr; i += WNT) {
+        for (int i = tid; i < nrows * gpr; i += NT) {
             const int ri = div_m(i, p.mG);
             const int g = i - ri * gpr;
             store_piece_at(lds + ((2 * ofr + ri) % NSLOT) * SB + (p.pw + 8 * g) * 8, load_piece(n, 2 * ofr - p.ph + ri, g));
@@ -591,7 +591,7 @@ hipError_t launch_c3p(const C3PParams &prm, const ConvGeom &g, size_t lds, hipSt
 {
     const hipError_t e = raise_lds_limit((const void *)conv_c3s2_ws_kernel<R>, (int)lds);
     if (e != hipSuccess) return e;
-    return launch(conv_c3s2_ws_kernel<R>, dim3(c3s2_grid(g)), dim3(WNT), (uint32_t)lds, st, nullptr, e1, prm);
+    return launch(conv_c3s2_ws_kernel<R>, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
 }
 
 }  // namespace
