@@ -392,7 +392,7 @@ def main():
                              "gbps": round(sum(kb2.values()) / (ms2 * 1e-3) / 1e9, 1),
                              "kernels": [kernel_entry("conv_fprop_stats(first layer)", st2[0],
                                                       kb2["conv_fprop_stats"], conv_flops(g2),
-                                                      ("train_stem", ["widen_filter", "conv_c3s2"])),
+                                                      ("train_stem", ["conv_c3s2"])),
                                          kernel_entry("bn_stats_finalize", st2[1], 0, 0),
                                          kernel_entry("bn_apply_relu_mask", st2[2], kb2["bn_apply_relu_mask"], 0,
                                                       ("train_stem", ["bn_apply_relu_mask"]))]}

@@ -78,7 +78,7 @@ ConvGeom cbr::dgrad_geom(const ConvGeom &g)
 
 namespace {
 
-struct TrainLayout { size_t partials, scale, shift, wexp, total; };
+struct TrainLayout { size_t partials, scale, shift, total; };
 struct InferLayout { size_t wfold, bfold, total; };
 struct BwdLayout { size_t dz, part, coef, wpart, wflip, total; };
 
@@ -89,7 +89,6 @@ TrainLayout train_layout(const ConvGeom &g, int plan)
     L.partials = o; o = align_up(o + sizeof(float) * (2 * g.K + 1) * (size_t)train_partial_rows(g, plan));
     L.scale = o; o = align_up(o + sizeof(float) * g.K);
     L.shift = o; o = align_up(o + sizeof(float) * g.K);
-    L.wexp = o; o = align_up(o + (plan == PLAN_FIRST_LAYER ? c3s2_wexp_bytes(g) : 0));
     L.total = o;
     return L;
 }
@@ -276,8 +275,7 @@ int cbr_forward_train_ev(const cbr_shape *shape, const uint16_t *x, const uint16
         plan == PLAN_PERSIST3X3
             ? launch_conv3x3_c64_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
         : plan == PLAN_FIRST_LAYER
-            ? launch_conv_c3s2_stats(g, x, w, (uint16_t *)ws_at(workspace, L.wexp), z, partials, s, ev(events, 0),
-                                     ev(events, 1))
+            ? launch_conv_c3s2_stats(g, x, w, z, partials, s, ev(events, 0), ev(events, 1))
             : launch_conv_fprop(g, EPI_STATS, plan, x, w, nullptr, z, partials, s, ev(events, 0), ev(events, 1));
     if (ec != hipSuccess) return CBR_E_HIP;
     if (launch_stats_finalize(train_partial_rows(g, plan), g.K, partials, fin, s, ev(events, 2), ev(events, 3)) !=

@@ -101,15 +101,14 @@ hipError_t launch_conv3x3_c64_stats(const ConvGeom &g, const uint16_t *x, const 
 
 // First-layer conv (3 input channels, stride 2, 64 output channels) + channel statistics:
 // persistent, one workgroup per CU over contiguous ranges of 128-pixel steps, MFMA and
-// epilogue waves specialised; pixels widened to 4 channels in an LDS ring of input rows;
-// the filter widened to [64][R][8][4] in workspace; one statistics row per workgroup
+// epilogue waves specialised; pixels widened to 4 channels in an LDS ring of input rows,
+// the filter to [64][R][8][4] in LDS by each workgroup; one statistics row per workgroup
 // (c3s2_grid rows).
 bool c3s2_eligible(const ConvGeom &g);
 int c3s2_grid(const ConvGeom &g);
 size_t c3s2_lds_bytes(const ConvGeom &g);
-size_t c3s2_wexp_bytes(const ConvGeom &g);
-hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *wexp,
-                                  uint16_t *z, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
+                                  float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 
 // Rows of per-channel partial statistics the training forward produces.  The partials
 // area holds R rows of [2][K] fp32 (each channel's mean over the row's output pixels,

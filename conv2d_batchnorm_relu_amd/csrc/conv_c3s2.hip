@@ -36,10 +36,10 @@ constexpr int MAXR = 7;    // filter rows
 
 struct C3PParams {
     const uint16_t *x;      // N x H x W x 3
-    const uint16_t *wexp;   // 64 x R x 8 x 4 (zero-padded filter)
+    const uint16_t *w;      // 64 x R x S x 3 (KRSC)
     uint16_t *z;            // N x P x Q x 64
     float *partials;        // [gridDim.x][2][64] means and M2, then [gridDim.x] counts
-    int N, H, W, R, ph, pw, P, Q;
+    int N, H, W, R, S, ph, pw, P, Q;
     int slot_bytes;         // LW * 8: widened pixels per staged row, zero columns included
     int nslot;              // ring slots
     int vpi;                // input rows an image spans: 2 (P - 1) + R
@@ -59,17 +59,6 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// Widened filter [64][R][8][4] <- KRSC [64][R][S][3], zeros elsewhere.
-__global__ __launch_bounds__(256) void widen_filter_c3_kernel(const uint16_t *__restrict__ w, int R, int S,
-                                                             uint16_t *__restrict__ wexp)
-{
-    const int total = HK * R * 32;
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-        const int c = i & 3, s = (i >> 2) & 7, kr = i >> 5;          // kr = k*R + r
-        wexp[i] = (c < 3 && s < S) ? w[((size_t)kr * S + s) * 3 + c] : (uint16_t)0;
-    }
 }
 
 // A block's fragment reads are inline assembly issued together, and each MFMA waits
@@ -208,6 +197,35 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_ws_kernel(C3PParams p)
         }
     }
 
+    // The widened filter [64][R][8][4] (element ((k R + r) 8 + s) 4 + c: taps s >= S and
+    // channel 3 zero), built by every thread from the KRSC filter in the second result
+    // buffer, which the MFMA waves first write in the range's second step: by then every
+    // MFMA wave has passed the first step's barrier, so has its fragments.  One 8-byte
+    // group (k, r, s) per iteration.
+    {
+        // every thread's groups gathered first (their loads all in flight), then stored
+        constexpr int NG = (HK * R * 8 + NT - 1) / NT;
+        uint8_t *const wl = accb + ACC_BYTES;
+        uint32_t lo[NG], hv[NG];
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int i = tid + NT * u, s8 = i & 7, kr = i >> 3;   // kr = k R + r
+            lo[u] = 0;
+            hv[u] = 0;
+            if (i < HK * R * 8 && s8 < p.S) {
+                const uint16_t *src = p.w + ((size_t)kr * p.S + s8) * 3;
+                lo[u] = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
+                hv[u] = src[2];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int i = tid + NT * u;
+            if (i < HK * R * 8) *(u32x2 *)(wl + i * 8) = u32x2{lo[u], hv[u]};
+        }
+    }
+    __syncthreads();
+
     // The step sequence, the same for both kinds of wave (each passes one barrier per step).
     struct StepIt {
         int n, s, img;
@@ -217,16 +235,17 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     if (mw) {
         // MFMA waves: the widened filter, both channel halves.  Fragment t of half j: lane
         // (l32, hi) holds output channel 32j + l32, tap row t / 2, taps 4 (t % 2) + 2 hi
-        // and + 1, four channels each: 16 bytes of wexp.
+        // and + 1, four channels each: 16 bytes of the widened filter.
         const int msimd = wave;
+        const uint8_t *const wl = accb + ACC_BYTES;
         bf16x8 w0[nks], w1[nks];
 #pragma unroll
         for (int t = 0; t < nks; ++t) {
-            w0[t] = *(const bf16x8 *)(p.wexp + ((size_t)l32 * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi);
-            w1[t] = *(const bf16x8 *)(p.wexp + ((size_t)(32 + l32) * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi);
+            w0[t] = *(const bf16x8 *)(wl + ((l32 * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi) * 2);
+            w1[t] = *(const bf16x8 *)(wl + (((32 + l32) * R + (t >> 1)) * 32 + 16 * (t & 1) + 8 * hi) * 2);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // every read of it done before the step loop's counted waits
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         int cbuf = 0;
         StepIt it = it0;
         for (int t = t0; t < t1; ++t, ++it.s) {
@@ -287,7 +306,6 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     // Epilogue waves: lane l holds channels 8 (l % 8) .. + 7 of pixels 8 r + l / 8 of its
     // 32-pixel quarter of a step.  Running statistics per lane: sums of deviations from a
     // shift (the lane's first value of each channel) and of their squares, and the count.
-    __syncthreads();
     const int ew = wave - NMW, c8 = lane & 7, et = tid - NMW * 64;
     float c[8], s1[8], s2[8], cnt = 0.f;
 #pragma unroll
@@ -587,11 +605,12 @@ C3Ring c3p_ring(const ConvGeom &g)
 }
 
 template <int R>
-hipError_t launch_c3p(const C3PParams &prm, const ConvGeom &g, size_t lds, hipStream_t st, hipEvent_t e1)
+hipError_t launch_c3p(const C3PParams &prm, const ConvGeom &g, size_t lds, hipStream_t st, hipEvent_t e0,
+                      hipEvent_t e1)
 {
     const hipError_t e = raise_lds_limit((const void *)conv_c3s2_ws_kernel<R>, (int)lds);
     if (e != hipSuccess) return e;
-    return launch(conv_c3s2_ws_kernel<R>, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, nullptr, e1, prm);
+    return launch(conv_c3s2_ws_kernel<R>, dim3(c3s2_grid(g)), dim3(NT), (uint32_t)lds, st, e0, e1, prm);
 }
 
 }  // namespace
@@ -624,23 +643,20 @@ size_t c3s2_lds_bytes(const ConvGeom &g)
     return std::max((size_t)c3p_ring(g).nslot * c3p_lw(g) * 8 + 2 * ACC_BYTES, (size_t)EST_BYTES);
 }
 
-size_t c3s2_wexp_bytes(const ConvGeom &g) { return (size_t)HK * g.R * 32 * 2; }
-
-hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *wexp,
-                                  uint16_t *z, float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const uint16_t *w, uint16_t *z,
+                                  float *partials, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    hipError_t e = launch(widen_filter_c3_kernel, dim3((HK * g.R * 32 + 255) / 256), dim3(256), 0, st, e0, nullptr, w,
-                          g.R, g.S, wexp);
-    if (e != hipSuccess) return e;
+    static_assert(HK * MAXR * 32 * 2 <= ACC_BYTES, "the widened filter fits one result buffer");
     C3PParams prm;
     prm.x = x;
-    prm.wexp = wexp;
+    prm.w = w;
     prm.z = z;
     prm.partials = partials;
     prm.N = g.N;
     prm.H = g.H;
     prm.W = g.W;
     prm.R = g.R;
+    prm.S = g.S;
     prm.ph = g.ph;
     prm.pw = g.pw;
     prm.P = g.P;
@@ -652,13 +668,13 @@ hipError_t launch_conv_c3s2_stats(const ConvGeom &g, const uint16_t *x, const ui
     prm.mG = (uint32_t)(((1ull << 32) + g.W / 8 - 1) / (g.W / 8));       // 0 for W = 8
     const size_t lds = c3s2_lds_bytes(g);
     switch (g.R) {
-    case 1: return launch_c3p<1>(prm, g, lds, st, e1);
-    case 2: return launch_c3p<2>(prm, g, lds, st, e1);
-    case 3: return launch_c3p<3>(prm, g, lds, st, e1);
-    case 4: return launch_c3p<4>(prm, g, lds, st, e1);
-    case 5: return launch_c3p<5>(prm, g, lds, st, e1);
-    case 6: return launch_c3p<6>(prm, g, lds, st, e1);
-    case 7: return launch_c3p<7>(prm, g, lds, st, e1);
+    case 1: return launch_c3p<1>(prm, g, lds, st, e0, e1);
+    case 2: return launch_c3p<2>(prm, g, lds, st, e0, e1);
+    case 3: return launch_c3p<3>(prm, g, lds, st, e0, e1);
+    case 4: return launch_c3p<4>(prm, g, lds, st, e0, e1);
+    case 5: return launch_c3p<5>(prm, g, lds, st, e0, e1);
+    case 6: return launch_c3p<6>(prm, g, lds, st, e0, e1);
+    case 7: return launch_c3p<7>(prm, g, lds, st, e0, e1);
     default: return hipErrorInvalidValue;   // not eligible
     }
 }

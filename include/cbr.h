@@ -167,7 +167,7 @@ int cbr_backward(const cbr_shape *shape,
  * then, with hipGetSymbolAddress).  The call itself allocates nothing.
  * Limit: shapes whose cbr_workspace_bytes(shape, CBR_OP_TRAIN) exceeds
  * CBR_NOALLOC_SCRATCH_BYTES return CBR_E_WORKSPACE (the 256 x 56 x 56 x 64 workload needs
- * about 133 KB, the 224 x 224 first layer at N = 64 about 161 KB).
+ * about 133 KB, the 224 x 224 first layer at N = 64 also about 133 KB).
  * All calls on one device share that device's array: calls that may overlap on one
  * device (different streams, different host threads) race, and must be serialised by
  * the caller.  A call leaves the array's contents undefined; no call depends on them.
