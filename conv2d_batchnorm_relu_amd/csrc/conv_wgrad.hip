@@ -542,7 +542,7 @@ __global__ __launch_bounds__(C::NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
         const int byte = 2 * (wn * 32 * NJ + 32 * j + 16 * (G & 1) + 4 * (li & 3));
         ba[j] = lbase + TR_STAGE_A + prow * TR_RSB + (byte ^ ((prow & 3) << 6));
     }
-    i16x4 af[2][MI][2], bf[2][NJ][2];
+    i16x4 af[3][MI][2], bf[3][NJ][2];
     auto read_frags = [&](i16x4 (&a)[MI][2], i16x4 (&b)[NJ][2], int t, int kh) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)((t % TR_NSTAGE) * TR_STAGE);
 #pragma unroll
@@ -580,42 +580,107 @@ __global__ __launch_bounds__(C::NT, 1) void conv_wgrad_tr_kernel(WgradTrParams p
         for (int j = 0; j < NJ; ++j) { tr_tie(b[j][0]); tr_tie(b[j][1]); }
     };
 
-    // Slice t lives in stage t % 3; slices t + 1 and t + 2 are in flight while it is used.
-    const int npro = min(TR_NSTAGE - 1, nsteps);
-    for (int t = 0; t < npro; ++t) dma_issue(t);
-    if (nsteps > 0) {
-        if (npro > 1) tr_vm_wait<TR_IPW>();
-        else tr_vm_wait<0>();
-        tr_barrier();
-        read_frags(af[0], bf[0], 0, 0);
-    }
-    for (int t = 0; t < nsteps; ++t) {
-#pragma unroll
-        for (int kh = 0; kh < 3; ++kh) {
-            read_frags(af[(kh + 1) & 1], bf[(kh + 1) & 1], t, kh + 1);
+    if constexpr (TR_NSTAGE == 3) {
+        // Three slices in LDS, the barrier in mid-slice (after k-step 1), fragment sets read
+        // two k-steps ahead, three sets rotating (k-step kh of slice t uses set (4t + kh) % 3).
+        // The mid-slice barrier of slice t publishes slice t + 1 (each wave waits for its own
+        // loads of it first) and shows every wave past slice t - 1, whose buffer then takes
+        // slice t + 2's loads.  Slice t + 1's first two fragment sets are read during k-steps
+        // 2 and 3 of slice t, so no k-step waits behind a barrier for its reads.
+        const int npro = min(2, nsteps);
+        for (int t = 0; t < npro; ++t) dma_issue(t);
+        if (nsteps > 0) {
+            if (npro > 1) tr_vm_wait<TR_IPW>();
+            else tr_vm_wait<0>();
+            tr_barrier();
+            read_frags(af[0], bf[0], 0, 0);
+            read_frags(af[1], bf[1], 0, 1);
+        }
+        auto slice = [&](int t, auto pc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int S0 = P % 3, S1 = (P + 1) % 3, S2 = (P + 2) % 3;   // k-step 3 uses S0 again
+            const bool more = t + 1 < nsteps;
+            // k-step 0
             tr_lgkm_wait<NRD>();
-            tie_set(af[kh & 1], bf[kh & 1]);
+            tie_set(af[S0], bf[S0]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma(af[kh & 1], bf[kh & 1]);
+            mfma(af[S0], bf[S0]);
             __builtin_amdgcn_sched_barrier(0);
-            if (kh == 0 && t + TR_NSTAGE - 1 < nsteps) dma_issue(t + TR_NSTAGE - 1);
+            read_frags(af[S2], bf[S2], t, 2);
+            // k-step 1
+            tr_lgkm_wait<NRD>();
+            tie_set(af[S1], bf[S1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(af[S1], bf[S1]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(af[S0], bf[S0], t, 3);
+            // mid-slice barrier (no LDS wait: the reads in flight are of slice t, and every
+            // read of slice t - 1 was waited for at its own k-steps)
+            if (more) tr_vm_wait<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 2 < nsteps) dma_issue(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            // k-step 2
+            tr_lgkm_wait<NRD>();
+            tie_set(af[S2], bf[S2]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(af[S2], bf[S2]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read_frags(af[S1], bf[S1], t + 1, 0);
+            // k-step 3
+            if (more) tr_lgkm_wait<NRD>();
+            else tr_lgkm_wait<0>();
+            tie_set(af[S0], bf[S0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(af[S0], bf[S0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read_frags(af[S2], bf[S2], t + 1, 1);
+        };
+        for (int t = 0; t < nsteps; t += 3) {
+            slice(t, std::integral_constant<int, 0>{});
+            if (t + 1 < nsteps) slice(t + 1, std::integral_constant<int, 1>{});
+            if (t + 2 < nsteps) slice(t + 2, std::integral_constant<int, 2>{});
+        }
+    } else {
+        // Slice t lives in stage t % 3; slices t + 1 and t + 2 are in flight while it is used.
+        const int npro = min(TR_NSTAGE - 1, nsteps);
+        for (int t = 0; t < npro; ++t) dma_issue(t);
+        if (nsteps > 0) {
+            if (npro > 1) tr_vm_wait<TR_IPW>();
+            else tr_vm_wait<0>();
+            tr_barrier();
+            read_frags(af[0], bf[0], 0, 0);
+        }
+        for (int t = 0; t < nsteps; ++t) {
+    #pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+                read_frags(af[(kh + 1) & 1], bf[(kh + 1) & 1], t, kh + 1);
+                tr_lgkm_wait<NRD>();
+                tie_set(af[kh & 1], bf[kh & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma(af[kh & 1], bf[kh & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kh == 0 && t + TR_NSTAGE - 1 < nsteps) dma_issue(t + TR_NSTAGE - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            tr_lgkm_wait<0>();
+            tie_set(af[1], bf[1]);
+            // slice t + 1 landed (with three stages slice t + 2 may stay in flight); every wave
+            // is past slice t
+            if constexpr (TR_NSTAGE == 3) {
+                if (t + 2 < nsteps) tr_vm_wait<TR_IPW>();
+                else if (t + 1 < nsteps) tr_vm_wait<0>();
+            } else {
+                if (t + 1 < nsteps) tr_vm_wait<0>();
+            }
+            tr_barrier();
+            if (t + 1 < nsteps) read_frags(af[0], bf[0], t + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(af[1], bf[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        tr_lgkm_wait<0>();
-        tie_set(af[1], bf[1]);
-        // slice t + 1 landed (with three stages slice t + 2 may stay in flight); every wave
-        // is past slice t
-        if constexpr (TR_NSTAGE == 3) {
-            if (t + 2 < nsteps) tr_vm_wait<TR_IPW>();
-            else if (t + 1 < nsteps) tr_vm_wait<0>();
-        } else {
-            if (t + 1 < nsteps) tr_vm_wait<0>();
-        }
-        tr_barrier();
-        if (t + 1 < nsteps) read_frags(af[0], bf[0], t + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma(af[1], bf[1]);
-        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Accumulator layout of v_mfma_f32_32x32x16: lane l holds column (l & 31) and rows
