@@ -105,11 +105,15 @@ def test_infer_conv_plan(g, plan):
 # runs the generic kernel, so the workspace must hold its partials.
 # Two more layers for the 256 x 256 transposed-read weight gradient (C % 256 == 0): two
 # output-channel tiles with a ragged last pixel split, and a 1x1 layer with two taps'
-# worth of channels per tile row.
+# worth of channels per tile row.  For the x-row offsets the transposed-read weight
+# gradient steps by 64 pixels per slice (row and image wraps): a vertical stride of 2 with
+# a 1x3 filter, and 5x3 images, where a step of 64 pixels crosses several images.
 @pytest.mark.parametrize("g", PLAN_GEOMS[:4] + [Geometry(2, 17, 13, 64, 64, 3, 3, 2, 1),
                                                 Geometry(30, 8, 16, 256, 256, 3, 3, 1, 1),
                                                 Geometry(7, 9, 11, 256, 512, 3, 3, 1, 1),
-                                                Geometry(3, 10, 10, 512, 256, 1, 1, 1, 0)], ids=str)
+                                                Geometry(3, 10, 10, 512, 256, 1, 1, 1, 0),
+                                                Geometry(3, 11, 9, 128, 256, 1, 3, 2, 0, stride_w=1, pad_w=1),
+                                                Geometry(5, 5, 3, 128, 256, 3, 3, 1, 1)], ids=str)
 def test_backward_plans(g, stage):
     want_dx = g.sh == 1 and g.sw == 1
     if stage == 2 and not want_dx:
