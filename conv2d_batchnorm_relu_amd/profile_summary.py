@@ -171,7 +171,7 @@ def write_md(res, path, command):
         f.write("\n".join(lines))
 
 
-def write_trace_md(stats_csv, path, command, note=""):
+def write_trace_md(stats_csv, path, command, note="", title="all bench workloads"):
     """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv: calls and
     average / min / max duration per kernel, longest total first."""
     rows = []
@@ -180,7 +180,7 @@ def write_trace_md(stats_csv, path, command, note=""):
             rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
                          float(r["MinNs"]), float(r["MaxNs"])))
     rows.sort(key=lambda r: -r[2])
-    lines = ["# Kernel durations, all bench workloads (rocprofv3 --kernel-trace --stats)", "",
+    lines = [f"# Kernel durations, {title} (rocprofv3 --kernel-trace --stats)", "",
              "Command (`<repo>` is the repository root, `<out>` the output directory):", "", "```",
              command.strip(), "```", "", f"Library sources sha256: `{sources_sha256()}`.", ""]
     if note:
@@ -200,9 +200,10 @@ def main(argv=None):
     ap.add_argument("--trace-stats", help="instead: summarise this kernel_stats.csv of a kernel-trace run")
     ap.add_argument("--note", default="", help="a paragraph added under the command (trace summaries)")
     ap.add_argument("--command", default="", help="the profiling command line(s), quoted in the summary")
+    ap.add_argument("--title", default="all bench workloads", help="what the traced run covered (trace summaries)")
     args = ap.parse_args(argv)
     if args.trace_stats:
-        write_trace_md(args.trace_stats, args.md, args.command, args.note)
+        write_trace_md(args.trace_stats, args.md, args.command, args.note, args.title)
         print(f"wrote {args.md}")
         return
     res = summarize(args.root)
