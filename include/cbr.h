@@ -18,7 +18,10 @@
  * gamma/beta, the weight gradient and conv bias are float32.
  *
  * Pointers: every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
- * caller; the library never allocates, frees or keeps device memory.  The cbr_shape
+ * caller; no call allocates or frees device memory.  The library keeps two things per
+ * device for the life of the process: the scratch array of cbr_forward_train_noalloc
+ * (module memory, loaded with the library) and, once cbr_backward has run with a dx
+ * there, a second stream with three events (created on that first call).  The cbr_shape
  * pointer is a host pointer read during the call only.  `workspace` is caller-owned
  * device scratch of at least cbr_workspace_bytes(shape, op) bytes (256-byte aligned);
  * its contents are undefined between calls and it must not be shared by calls that
