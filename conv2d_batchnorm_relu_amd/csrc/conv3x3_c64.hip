@@ -259,21 +259,29 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
         __builtin_amdgcn_raw_buffer_store_b128(sd.d[k], sd.zr, q * 1024 + ln * 16, 0, Z_POLICY);
     };
 
-    // The filter half into registers, through LDS: global-to-LDS loads put 16-byte chunk
-    // c of filter row r (KRSC: 72 chunks per output channel) at F + (64c + r) * 16, past
-    // the first step's ring slots (in slots the first k-loop has not loaded yet and in
-    // the staging buffers).  Load c gathers chunk c of all 64 rows (lane r), so the
-    // fragment reads below are conflict-free.  Fragment t of lane (l32, hi) is output
-    // channel 32j + l32, tap t / 4, input channels 16 (t % 4) + 8 hi .. + 7: chunk
-    // 8 (t / 4) + 2 (t % 4) + hi.  When the range starts at an image's first step, that
-    // step's rows stream into slots 0 .. rows0 - 1 meanwhile, and the filter sits past
-    // them; a range starting inside an image stages the filter at the start of LDS first
-    // and its first step's rows once the filter is in registers.
+    // The filter half into registers, through LDS, past the first step's ring slots (in
+    // slots the first k-loop has not loaded yet and in the staging buffers).  Filter row r
+    // (output channel; KRSC: 72 chunks of 16 bytes, 1152 bytes, nine cache lines) has its
+    // chunks in groups of eight, one cache line each.  Global-to-LDS load i moves line
+    // i % 9 of rows 8 (i / 9) .. + 7: lane l takes row 8 (i / 9) + l / 8 and chunk
+    // 8 (i % 9) + fsw(row, l % 8), so each load reads eight whole lines, and LDS
+    // position 16 l of load i holds that chunk.  fsw(r, q) = q ^ (r % 8) ^ ((r / 8) % 2)
+    // spreads the fragment reads below over the banks: their 16 lanes of rows
+    // 8b .. 8b + 15 and one chunk land in 16 distinct 16-byte bank slots.  Fragment t of
+    // lane (l32, hi) is output channel 32j + l32, tap t / 4, input channels
+    // 16 (t % 4) + 8 hi .. + 7: chunk 8 (t / 4) + 2 (t % 4) + hi.  When the range starts
+    // at an image's first step, that step's rows stream into slots 0 .. rows0 - 1
+    // meanwhile, and the filter sits past them; a range starting inside an image stages
+    // the filter at the start of LDS first and its first step's rows once the filter is
+    // in registers.
     const bool at_start = s_first == 0;
     const int F = at_start ? rows0 * SLOT : 0;
-    for (int c = wave; c < 72; c += NW)
-        __builtin_amdgcn_global_load_lds((const void *)(p.w + ((size_t)lane * 72 + c) * 8), (lds_u8 *)lds + F + c * 1024,
+    for (int i = wave; i < 72; i += NW) {
+        const int row = 8 * (i / 9) + (lane >> 3);
+        const int ch = 8 * (i % 9) + ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1));
+        __builtin_amdgcn_global_load_lds((const void *)(p.w + ((size_t)row * 72 + ch) * 8), (lds_u8 *)lds + F + i * 1024,
                                          16, 0, 0);
+    }
     const int zrows = at_start ? rows0 : 0;   // slots whose padding columns are zeroed now
     for (int c = tid; c < zrows * 16; c += NT) {
         const int slot = c >> 4, col = (c & 8) ? W + 1 : 0;
@@ -285,7 +293,8 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_c64_stats_kernel(HaloParams p)
     bf16x8 wf[KSTEPS];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t)
-        wf[t] = *(const bf16x8 *)(lds + F + (((t >> 2) * 8 + (t & 3) * 2 + hi) * 64 + 32 * j + l32) * 16);
+        wf[t] = *(const bf16x8 *)(lds + F + ((4 * j + (l32 >> 3)) * 9 + (t >> 2)) * 1024 +
+                                  (8 * (l32 & 7) + ((2 * (t & 3) + hi) ^ (l32 & 7) ^ ((l32 >> 3) & 1))) * 16);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // the filter area is free again
     // The padding columns of the other slots zeroed (the k-loops' row loads fill the
