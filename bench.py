@@ -153,6 +153,9 @@ def main():
                     help="images of the headline workload the CPU oracle runs (of 256)")
     ap.add_argument("--cold", type=int, default=5, help="steps timed after evicting the caches")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-box copy and matmul peak runs")
+    ap.add_argument("--batch-sweep", default="",
+                    help="comma-separated batch sizes <= 256: time the headline layer's conv at each (the "
+                         "first images of the headline input) and fit it against the steps per workgroup")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device three times (the known-size "
                          "copy that scales HBM byte counters)")
@@ -289,6 +292,32 @@ def main():
         "kernel_ms_spread": {e["kernel"]: spread(v) for e, v in zip(kernels, per)},
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
     }
+    if args.batch_sweep:
+        # The persistent conv gives each workgroup a contiguous range of 256-pixel steps
+        # (13 per 56x56 image); its time is about a fixed part plus a cost per step of the
+        # busiest workgroup.
+        spi = -(-g.h * g.w // 256)
+        rows = []
+        lib = cbr._load()
+        lib.cbr_set_plan_override(0, 1)   # the persistent conv at every batch size
+        for nb in (int(v) for v in args.batch_sweep.split(",")):
+            assert 1 <= nb <= g.n, f"--batch-sweep sizes must lie in 1..{g.n}"
+            spn = cbr.make_shape(nb, g.h, g.w, g.c, g.k, g.r, g.s, g.sh, g.ph, stride_w=g.sw, pad_w=g.pw)
+
+            def sweep_step(events):
+                cbr.cbr_forward_train(spn, x[:nb], w, gamma, beta, rm, rv, wl.eps, wl.momentum, z[:nb], y[:nb],
+                                      mask[:cbr.cbr_mask_words(spn)], sm, si, rmo, rvo, ws, events=events)
+
+            msn, stn, pern = timed(sweep_step, 6, 40, 10)
+            tot = nb * spi
+            rows.append({"n": nb, "max_steps_per_workgroup": -(-tot // min(tot, 256)),
+                         "conv_us": round(pct(pern[0], 50) * 1e3, 2), "call_us": round(msn * 1e3, 2)})
+            log(f"batch sweep N = {nb}: conv {rows[-1]['conv_us']} us")
+        lib.cbr_set_plan_override(0, 0)
+        slope, icpt = np.polyfit([r["max_steps_per_workgroup"] for r in rows], [r["conv_us"] for r in rows], 1)
+        out["batch_sweep"] = {"workload": "headline layer's conv at batch n (median of 40 calls)", "rows": rows,
+                              "fit_conv_us": {"fixed": round(float(icpt), 2), "per_step": round(float(slope), 3)}}
+
     del z, y, mask, ws, x
     torch.cuda.empty_cache()
 
