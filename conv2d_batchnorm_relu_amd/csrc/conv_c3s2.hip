@@ -320,7 +320,8 @@ __global__ __launch_bounds__(NT, 1) void conv_c3s2_ws_kernel(C3PParams p)
     constexpr int Z_POLICY = 16;
     // Step (n_, a_, npix_)'s results in buffer buf: statistics, bf16 z to global memory.
     // Every row of the buffer holds a value of each channel (pixels past the step were
-    // computed as the step's first pixel), so the shifts set from round 0 are valid.
+    // computed as the step's first pixel), so the shifts set from the first finished step
+    // are valid.
     auto finish_t = [&](auto masked, int buf, int n_, int a_, int npix_) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
         const uint8_t *ab = accb + buf * ACC_BYTES;

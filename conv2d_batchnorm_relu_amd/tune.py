@@ -9,7 +9,7 @@ eligible (cbr_plan_eligible), forcing it with cbr_set_plan_override, and keeps t
 fastest.  It writes the table that csrc/cbr_plan.cpp compiles in (cbr_tune_table.inc)
 and a markdown summary of every timing.  Rebuild the library after replacing the table.
 
-    python -m conv2d_batchnorm_relu_amd.tune --out-dir gpurun_out/tune [--batch 32 256] [--reps 10]
+    python -m conv2d_batchnorm_relu_amd.tune --out-dir <out> [--batch 32 256] [--reps 10]
         [--match '56x56 64->64 3x3'] [--stages 0 1]
 
 A stage's plans are compared by the time of the whole call that contains the stage (the
@@ -56,7 +56,7 @@ def vgg16_layers():
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--out-dir", default="gpurun_out/tune")
+    ap.add_argument("--out-dir", default="tune_out")
     ap.add_argument("--batch", type=int, nargs="+", default=[32, 256])
     ap.add_argument("--vgg-batch", type=int, nargs="*", default=[32])
     ap.add_argument("--reps", type=int, default=10)
@@ -140,7 +140,7 @@ def main(argv=None):
             cands = [p for p in plans if lib.cbr_plan_eligible(ctypes.byref(sp), stage, p) == 1]
             default = lib.cbr_plan_of(ctypes.byref(sp), stage)
             times = {}
-            # a stage's plan is judged by the whole call that contains it, timed over
+            # a stage's plan is rated by the whole call that contains it, timed over
             # back-to-back calls (the GPU's time per call, not the host's enqueue time)
             fn = run_train if stage == 0 else run_infer if stage == 1 else run_bwd if stage < 4 else run_bwd_nodz
             for plan in cands:
